@@ -1,0 +1,331 @@
+"""Thin ctypes binding of libcoda.so (include/coda.h), one function per C entry point.
+
+The functions marshal torch tensors into pointers, sizes and the current HIP
+stream and call the C library; every step of the computation runs in the HIP
+kernels.  Torch is used only to allocate device memory for outputs that the
+caller did not pass.  If the library is missing, every call raises: there is
+no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcoda.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "coda.h")
+
+_lib = None
+
+P = ctypes.c_void_p
+I = ctypes.c_int
+F = ctypes.c_float
+SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes), following include/coda.h
+_SIGS = {
+    "coda_status_str": (ctypes.c_char_p, [I]),
+    "coda_version": (ctypes.c_char_p, []),
+    "coda_nparts": (I, [I]),
+    "coda_mparts": (I, [I]),
+    "coda_lmhead_ce_workspace": (SZ, [I, I]),
+    "coda_lmhead_ce_bwd_workspace": (SZ, [I, I, I]),
+    "coda_gemm": (I, [P, I, P, I, P, I, I, I, I, P]),
+    "coda_gemm_res_sumsq": (I, [P, I, P, I, P, I, P, P, I, P, I, P, I, I, I, P]),
+    "coda_row_rms": (I, [P, I, I, I, F, P, P]),
+    "coda_gemm_rowscale": (I, [P, I, P, I, P, P, I, I, I, I, P]),
+    "coda_gemm_rope": (I, [P, I, P, I, P, P, F, I, I, P, I, I, I, I, P]),
+    "coda_gemm_rope_bwd": (I, [P, I, P, I, P, P, F, I, I, P, I, I, I, I, P]),
+    "coda_gemm_swiglu": (I, [P, I, P, I, P, P, I, P, I, I, I, I, P]),
+    "coda_lmhead_ce": (I, [P, I, P, I, P, P, P, P, P, SZ, I, I, I, P]),
+    "coda_gemm_swiglu_bwd": (I, [P, I, P, I, P, I, P, I, P, I, I, I, P]),
+    "coda_row_rms_bwd": (I, [P, I, I, I, P, P]),
+    "coda_gemm_rowscale_bwd": (I, [P, I, P, I, P, I, P, P, P, P, I, P, I, P, I, P, I, I, I, P]),
+    "coda_col_reduce": (I, [P, I, I, P, P]),
+    "coda_gemm_res_sumsq_bwd": (I, [P, I, P, I, P, I, P, I, P, I, P, I, I, I, I, P]),
+    "coda_gemm_wgrad": (I, [P, I, P, I, P, I, I, I, I, I, P]),
+    "coda_lmhead_ce_bwd": (I, [P, I, P, I, P, P, F, P, I, P, I, P, SZ, I, I, I, P]),
+}
+
+STATUS = {0: "CODA_OK", 1: "CODA_ERR_NULL", 2: "CODA_ERR_SHAPE", 3: "CODA_ERR_ALIGN",
+          4: "CODA_ERR_UNSUPPORTED", 5: "CODA_ERR_HIP", 6: "CODA_ERR_WORKSPACE"}
+
+
+class CodaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status_str(status)})")
+
+
+def lib():
+    """Load libcoda.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run gemm_epilogue_transformer_mainloop_amd/build.py")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/coda.h declares."""
+    with open(HEADER_PATH) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(coda_[a-z0-9_]+)\s*\(", src)))
+
+
+def status_str(s: int) -> str:
+    return lib().coda_status_str(s).decode()
+
+
+def _call(name, *args):
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise CodaError(name, st)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ld(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else int(t.stride(0))
+
+
+def _mat(t, dtype=torch.bfloat16, name="tensor"):
+    if t is None:
+        return None
+    if t.dtype != dtype or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name}: need a row-major 2-D {dtype} tensor, got {t.dtype} {tuple(t.shape)} {t.stride()}")
+    return t
+
+
+def _dense(t, name):
+    """Partials and vectors have no leading dimension in the ABI: they must be dense."""
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous (the C ABI takes no leading dimension for it)")
+    return t
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# ----------------------------------------------------------------------------
+# queries
+# ----------------------------------------------------------------------------
+
+
+def coda_nparts(N: int) -> int:
+    return int(lib().coda_nparts(N))
+
+
+def coda_mparts(M: int) -> int:
+    return int(lib().coda_mparts(M))
+
+
+def coda_lmhead_ce_workspace(M: int, V: int) -> int:
+    return int(lib().coda_lmhead_ce_workspace(M, V))
+
+
+def coda_lmhead_ce_bwd_workspace(M: int, V: int, d: int) -> int:
+    return int(lib().coda_lmhead_ce_bwd_workspace(M, V, d))
+
+
+# ----------------------------------------------------------------------------
+# forward
+# ----------------------------------------------------------------------------
+
+
+def coda_gemm(X, W, Y=None):
+    _mat(X, name="X"), _mat(W, name="W")
+    M, K = X.shape
+    N = W.shape[1]
+    if Y is None:
+        Y = _empty((M, N), torch.bfloat16, X)
+    _call("coda_gemm", _ptr(X), _ld(X), _ptr(W), _ld(W), _ptr(Y), _ld(Y), M, N, K, _stream())
+    return Y
+
+
+def coda_gemm_res_sumsq(X, W, Z=None, gamma=None, U=None, H2=None, part=None, want_h2=True, want_part=True):
+    M, K = X.shape
+    N = W.shape[1]
+    if U is None:
+        U = _empty((M, N), torch.bfloat16, X)
+    if H2 is None and want_h2 and gamma is not None:
+        H2 = _empty((M, N), torch.bfloat16, X)
+    if part is None and want_part:
+        part = _empty((M, coda_nparts(N)), torch.float32, X)
+    _dense(part, "part")
+    _call("coda_gemm_res_sumsq", _ptr(X), _ld(X), _ptr(W), _ld(W), _ptr(Z), _ld(Z), _ptr(gamma),
+          _ptr(U), _ld(U), _ptr(H2), _ld(H2), _ptr(part), M, N, K, _stream())
+    return U, H2, part
+
+
+def coda_row_rms(part, d: int, eps: float, r=None):
+    _dense(part, "part")
+    M, np_ = part.shape
+    if r is None:
+        r = _empty((M,), torch.float32, part)
+    _call("coda_row_rms", _ptr(part), np_, M, d, ctypes.c_float(eps), _ptr(r), _stream())
+    return r
+
+
+def coda_gemm_rowscale(A, W, r, Y=None):
+    M, K = A.shape
+    N = W.shape[1]
+    if Y is None:
+        Y = _empty((M, N), torch.bfloat16, A)
+    _call("coda_gemm_rowscale", _ptr(A), _ld(A), _ptr(W), _ld(W), _ptr(r), _ptr(Y), _ld(Y), M, N, K, _stream())
+    return Y
+
+
+def _rope(name, A, W, r, pos, theta, head_dim, n_rope, Y):
+    M, K = A.shape
+    N = W.shape[1]
+    if Y is None:
+        Y = _empty((M, N), torch.bfloat16, A)
+    _call(name, _ptr(A), _ld(A), _ptr(W), _ld(W), _ptr(r), _ptr(pos), ctypes.c_float(theta), head_dim,
+          n_rope, _ptr(Y), _ld(Y), M, N, K, _stream())
+    return Y
+
+
+def coda_gemm_rope(A, W, r, pos, theta: float, head_dim: int, n_rope: int, Y=None):
+    return _rope("coda_gemm_rope", A, W, r, pos, theta, head_dim, n_rope, Y)
+
+
+def coda_gemm_rope_bwd(A, W, r, pos, theta: float, head_dim: int, n_rope: int, Y=None):
+    return _rope("coda_gemm_rope_bwd", A, W, r, pos, theta, head_dim, n_rope, Y)
+
+
+def coda_gemm_swiglu(A, Wgu, r=None, Act=None, Pre=None, want_pre=True):
+    M, K = A.shape
+    F = Wgu.shape[1] // 2
+    if Act is None:
+        Act = _empty((M, F), torch.bfloat16, A)
+    if Pre is None and want_pre:
+        Pre = _empty((M, 2 * F), torch.bfloat16, A)
+    _call("coda_gemm_swiglu", _ptr(A), _ld(A), _ptr(Wgu), _ld(Wgu), _ptr(r), _ptr(Act), _ld(Act), _ptr(Pre),
+          _ld(Pre), M, F, K, _stream())
+    return Act, Pre
+
+
+def coda_lmhead_ce(H, W, labels, lse=None, loss_row=None, loss_mean=None, ws=None):
+    M, d = H.shape
+    V = W.shape[1]
+    if lse is None:
+        lse = _empty((M,), torch.float32, H)
+    if loss_row is None:
+        loss_row = _empty((M,), torch.float32, H)
+    if loss_mean is None:
+        loss_mean = _empty((1,), torch.float32, H)
+    if ws is None:
+        ws = _empty((max(coda_lmhead_ce_workspace(M, V), 16),), torch.uint8, H)
+    _call("coda_lmhead_ce", _ptr(H), _ld(H), _ptr(W), _ld(W), _ptr(labels), _ptr(lse), _ptr(loss_row),
+          _ptr(loss_mean), _ptr(ws), ws.numel() * ws.element_size(), M, V, d, _stream())
+    return lse, loss_row, loss_mean
+
+
+# ----------------------------------------------------------------------------
+# backward
+# ----------------------------------------------------------------------------
+
+
+def coda_gemm_swiglu_bwd(dOut, Wd, Pre, dPre=None, spart=None, want_spart=True):
+    M, N = dOut.shape
+    F = Wd.shape[0]
+    if dPre is None:
+        dPre = _empty((M, 2 * F), torch.bfloat16, dOut)
+    if spart is None and want_spart:
+        spart = _empty((M, coda_nparts(F)), torch.float32, dOut)
+    _dense(spart, "spart")
+    _call("coda_gemm_swiglu_bwd", _ptr(dOut), _ld(dOut), _ptr(Wd), _ld(Wd), _ptr(Pre), _ld(Pre), _ptr(dPre),
+          _ld(dPre), _ptr(spart), M, F, N, _stream())
+    return dPre, spart
+
+
+def coda_row_rms_bwd(spart, d: int, s=None):
+    _dense(spart, "spart")
+    M, np_ = spart.shape
+    if s is None:
+        s = _empty((M,), torch.float32, spart)
+    _call("coda_row_rms_bwd", _ptr(spart), np_, M, d, _ptr(s), _stream())
+    return s
+
+
+def coda_gemm_rowscale_bwd(dY, W1, U, gamma, r, s, dRes=None, dU=None, N2=None, gpart=None, want_n2=True,
+                           want_gpart=True):
+    M, N = dY.shape
+    d = W1.shape[0]
+    if dU is None:
+        dU = _empty((M, d), torch.bfloat16, dY)
+    if N2 is None and want_n2:
+        N2 = _empty((M, d), torch.bfloat16, dY)
+    if gpart is None and want_gpart:
+        gpart = _empty((coda_mparts(M), d), torch.float32, dY)
+    _dense(gpart, "gpart")
+    _call("coda_gemm_rowscale_bwd", _ptr(dY), _ld(dY), _ptr(W1), _ld(W1), _ptr(U), _ld(U), _ptr(gamma), _ptr(r),
+          _ptr(s), _ptr(dRes), _ld(dRes), _ptr(dU), _ld(dU), _ptr(N2), _ld(N2), _ptr(gpart), M, d, N, _stream())
+    return dU, N2, gpart
+
+
+def coda_col_reduce(gpart, dgamma=None):
+    _dense(gpart, "gpart")
+    mp, d = gpart.shape
+    if dgamma is None:
+        dgamma = _empty((d,), torch.float32, gpart)
+    _call("coda_col_reduce", _ptr(gpart), mp, d, _ptr(dgamma), _stream())
+    return dgamma
+
+
+def coda_gemm_res_sumsq_bwd(dU, W, X=None, dRes=None, dX=None, dW=None, want_dw=True):
+    M, N = dU.shape
+    K = W.shape[0]
+    if dX is None:
+        dX = _empty((M, K), torch.bfloat16, dU)
+    if dW is None and want_dw and X is not None:
+        dW = _empty((K, N), torch.float32, dU)
+    _call("coda_gemm_res_sumsq_bwd", _ptr(dU), _ld(dU), _ptr(W), _ld(W), _ptr(X), _ld(X), _ptr(dRes), _ld(dRes),
+          _ptr(dX), _ld(dX), _ptr(dW), _ld(dW), M, N, K, _stream())
+    return dX, dW
+
+
+def coda_gemm_wgrad(X, dY, dW=None, accumulate=False):
+    M, K = X.shape
+    N = dY.shape[1]
+    if dW is None:
+        dW = _empty((K, N), torch.float32, X)
+    _call("coda_gemm_wgrad", _ptr(X), _ld(X), _ptr(dY), _ld(dY), _ptr(dW), _ld(dW), M, K, N, int(bool(accumulate)),
+          _stream())
+    return dW
+
+
+def coda_lmhead_ce_bwd(H, W, labels, lse, grad_scale: float, dH=None, dW=None, ws=None, ws_rows=None):
+    M, d = H.shape
+    V = W.shape[1]
+    if dH is None:
+        dH = _empty((M, d), torch.bfloat16, H)
+    if dW is None:
+        dW = _empty((d, V), torch.float32, H)
+    if ws is None:
+        rows = M if ws_rows is None else ws_rows
+        ws = _empty((max(rows * V * 2, coda_lmhead_ce_bwd_workspace(M, V, d), 16),), torch.uint8, H)
+    _call("coda_lmhead_ce_bwd", _ptr(H), _ld(H), _ptr(W), _ld(W), _ptr(labels), _ptr(lse),
+          ctypes.c_float(grad_scale), _ptr(dH), _ld(dH), _ptr(dW), _ld(dW), _ptr(ws), ws.numel() * ws.element_size(),
+          M, V, d, _stream())
+    return dH, dW

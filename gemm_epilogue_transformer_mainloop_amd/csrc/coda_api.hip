@@ -1,0 +1,601 @@
+// coda_api.hip - C ABI of libcoda.so: argument validation, kernel selection
+// and launch of the fused GEMM-epilogue kernels and the auxiliary reductions.
+//
+// Every entry point validates its arguments before any HIP call, launches on
+// the caller's stream and returns; nothing is allocated or synchronised.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/coda.h"
+#include "coda_epilogues.hpp"
+
+using namespace coda;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Auxiliary reductions (fixed order, one thread per output element)
+// ---------------------------------------------------------------------------
+
+// r_i = 1/sqrt(sum_p part[i,p]/d + eps)  (paper Figure 4 / Figure 5 caption)
+__global__ void row_rms_kernel(const float* __restrict__ part, int nparts, int M, float inv_d,
+                               float eps, float* __restrict__ r) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M) return;
+  const float* p = part + (size_t)i * nparts;
+  float s = 0.0f;
+  for (int j = 0; j < nparts; ++j) s += p[j];
+  r[i] = 1.0f / sqrtf(s * inv_d + eps);
+}
+
+// s_i = sum_p spart[i,p] / d  (reading notes section 3)
+__global__ void row_sum_scale_kernel(const float* __restrict__ part, int nparts, int M, float inv_d,
+                                     float* __restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M) return;
+  const float* p = part + (size_t)i * nparts;
+  float s = 0.0f;
+  for (int j = 0; j < nparts; ++j) s += p[j];
+  out[i] = s * inv_d;
+}
+
+// dgamma_j = sum_q gpart[q, j]
+__global__ void col_reduce_kernel(const float* __restrict__ gpart, int mparts, int d,
+                                  float* __restrict__ out) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= d) return;
+  float s = 0.0f;
+  for (int q = 0; q < mparts; ++q) s += gpart[(size_t)q * d + j];
+  out[j] = s;
+}
+
+// Merge of per-tile (max, sum exp) into lse and the row loss (notes sec. 2).
+__global__ void ce_reduce_kernel(const float* __restrict__ pm, const float* __restrict__ ps,
+                                 const float* __restrict__ tgt, const int32_t* __restrict__ labels,
+                                 int nparts, int M, int V, float* __restrict__ lse,
+                                 float* __restrict__ loss) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M) return;
+  const float* m = pm + (size_t)i * nparts;
+  const float* s = ps + (size_t)i * nparts;
+  float L = -INFINITY;
+  for (int j = 0; j < nparts; ++j) L = fmaxf(L, m[j]);
+  float S = 0.0f;
+  for (int j = 0; j < nparts; ++j) S += s[j] * expf(m[j] - L);
+  const float l = L + logf(S);
+  lse[i] = l;
+  const int y = labels[i];
+  loss[i] = (y >= 0 && y < V) ? (l - tgt[i]) : __builtin_nanf("");
+}
+
+// Deterministic mean of the row losses: one workgroup, fixed-order tree.
+__global__ void __launch_bounds__(1024) mean_kernel(const float* __restrict__ x, int M,
+                                                    float* __restrict__ out) {
+  __shared__ float sh[1024];
+  float s = 0.0f;
+  for (int i = threadIdx.x; i < M; i += 1024) s += x[i];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = sh[0] / (float)M;
+}
+
+// ---------------------------------------------------------------------------
+// Validation helpers
+// ---------------------------------------------------------------------------
+
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Check {
+  coda_status st = CODA_OK;
+  void need(const void* p) {
+    if (st == CODA_OK && p == nullptr) st = CODA_ERR_NULL;
+  }
+  // A bf16 matrix of `rows` x `cols`, leading dimension ld (NULL allowed when
+  // optional or when it has no rows).
+  void bmat(const void* p, int ld, int cols, bool required = true, int rows = 1) {
+    if (st != CODA_OK) return;
+    if (p == nullptr) {
+      if (required && rows > 0) st = CODA_ERR_NULL;
+      return;
+    }
+    if (ld < cols || ld <= 0) { st = CODA_ERR_SHAPE; return; }
+    if (!al16(p) || (ld % 8) != 0) st = CODA_ERR_ALIGN;
+  }
+  void fmat(const void* p, int ld, int cols, bool required = true, int rows = 1) {
+    if (st != CODA_OK) return;
+    if (p == nullptr) {
+      if (required && rows > 0) st = CODA_ERR_NULL;
+      return;
+    }
+    if (ld < cols || ld <= 0) { st = CODA_ERR_SHAPE; return; }
+    if (!al16(p) || (ld % 4) != 0) st = CODA_ERR_ALIGN;
+  }
+  void vec(const void* p, bool required = true, bool aligned16 = false, int n = 1) {
+    if (st != CODA_OK) return;
+    if (p == nullptr) {
+      if (required && n > 0) st = CODA_ERR_NULL;
+      return;
+    }
+    if (aligned16 && !al16(p)) st = CODA_ERR_ALIGN;
+  }
+  void shape(bool ok) {
+    if (st == CODA_OK && !ok) st = CODA_ERR_SHAPE;
+  }
+  void unsupported(bool ok) {
+    if (st == CODA_OK && !ok) st = CODA_ERR_UNSUPPORTED;
+  }
+};
+
+// One gfx950 check per device, cached (architecture never changes).
+std::atomic<int> g_arch_ok[64];
+
+coda_status device_ok() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CODA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return CODA_ERR_UNSUPPORTED;
+  int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return CODA_ERR_HIP;
+    v = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_ok[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? CODA_OK : CODA_ERR_UNSUPPORTED;
+}
+
+coda_status launched() { return hipGetLastError() == hipSuccess ? CODA_OK : CODA_ERR_HIP; }
+
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Launch one fused GEMM: features F (output columns), tokens T (output rows).
+template <bool WK, bool XK, int BT = 256, class Epi>
+coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, int F, int T, int K,
+                        const Epi& epi, hipStream_t stream) {
+  constexpr int BF = 256;
+  Problem p;
+  p.W = W;
+  p.X = X;
+  p.ldw = ldw;
+  p.ldx = ldx;
+  p.F = F;
+  p.T = T;
+  p.K = K;
+  p.nTF = cdiv(F, BF);
+  p.nTT = cdiv(T, BT);
+  const int nb = p.nTF * p.nTT;
+  if (nb == 0) return CODA_OK;
+  hipLaunchKernelGGL((gemm_epi_kernel<BF, BT, WK, XK, Epi>), dim3(nb), dim3(NT), 0, stream, p, epi);
+  return launched();
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+
+extern "C" {
+
+const char* coda_status_str(coda_status s) {
+  switch (s) {
+    case CODA_OK: return "ok";
+    case CODA_ERR_NULL: return "a required pointer is NULL";
+    case CODA_ERR_SHAPE: return "invalid size or leading dimension";
+    case CODA_ERR_ALIGN: return "pointer or leading dimension misaligned";
+    case CODA_ERR_UNSUPPORTED: return "unsupported device or parameter combination";
+    case CODA_ERR_HIP: return "HIP runtime error";
+    case CODA_ERR_WORKSPACE: return "workspace missing or too small";
+  }
+  return "unknown status";
+}
+
+const char* coda_version(void) { return "coda-gfx950 0.1"; }
+
+int coda_nparts(int N) { return N <= 0 ? 0 : cdiv(N, WAVE_F); }
+int coda_mparts(int M) { return M <= 0 ? 0 : cdiv(M, WAVE_T); }
+
+size_t coda_lmhead_ce_workspace(int M, int V) {
+  if (M <= 0 || V <= 0) return 0;
+  const size_t np = (size_t)coda_nparts(V);
+  return (2 * (size_t)M * np + 2 * (size_t)M) * sizeof(float);
+}
+
+static const int kCeBwdMinRows = 256;
+
+size_t coda_lmhead_ce_bwd_workspace(int M, int V, int d) {
+  (void)d;
+  if (M <= 0 || V <= 0) return 0;
+  const size_t rows = (size_t)(M < kCeBwdMinRows ? M : kCeBwdMinRows);
+  return rows * (size_t)V * 2;
+}
+
+coda_status coda_gemm(const coda_bf16* X, int ldx, const coda_bf16* W, int ldw, coda_bf16* Y,
+                      int ldy, int M, int N, int K, hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && N >= 0 && K >= 0);
+  c.bmat(X, ldx, K, true, M);
+  c.bmat(W, ldw, N);
+  c.bmat(Y, ldy, N, true, M);
+  c.shape(N % 8 == 0 && K % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (M == 0 || N == 0) return CODA_OK;
+  if (coda_status s = device_ok()) return s;
+  EpiLinear<false, false> e{nullptr, nullptr, 0, Y, ldy};
+  return launch_gemm<false, true>(W, ldw, X, ldx, N, M, K, e, stream);
+}
+
+coda_status coda_gemm_res_sumsq(const coda_bf16* X, int ldx, const coda_bf16* W, int ldw,
+                                const coda_bf16* Z, int ldz, const coda_bf16* gamma, coda_bf16* U,
+                                int ldu, coda_bf16* H2, int ldh, float* part, int M, int N, int K,
+                                hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && N >= 0 && K >= 0);
+  c.bmat(X, ldx, K, true, M);
+  c.bmat(W, ldw, N);
+  c.bmat(Z, ldz, N, false, M);
+  c.bmat(U, ldu, N, true, M);
+  c.bmat(H2, ldh, N, false, M);
+  if (H2) c.vec(gamma, true, true);
+  c.vec(part, false, false, M);
+  c.shape(N % 8 == 0 && K % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (M == 0 || N == 0) return CODA_OK;
+  if (coda_status s = device_ok()) return s;
+  const int np = coda_nparts(N);
+#define CODA_RS(HZ, HH, HP)                                                              \
+  {                                                                                      \
+    EpiResSumsq<HZ, HH, HP> e{Z, ldz, gamma, U, ldu, H2, ldh, part, np};                 \
+    return launch_gemm<false, true>(W, ldw, X, ldx, N, M, K, e, stream);                 \
+  }
+  const bool hz = Z != nullptr, hh = H2 != nullptr, hp = part != nullptr;
+  if (hz && hh && hp) CODA_RS(true, true, true)
+  if (hz && hh && !hp) CODA_RS(true, true, false)
+  if (hz && !hh && hp) CODA_RS(true, false, true)
+  if (hz && !hh && !hp) CODA_RS(true, false, false)
+  if (!hz && hh && hp) CODA_RS(false, true, true)
+  if (!hz && hh && !hp) CODA_RS(false, true, false)
+  if (!hz && !hh && hp) CODA_RS(false, false, true)
+  CODA_RS(false, false, false)
+#undef CODA_RS
+}
+
+coda_status coda_row_rms(const float* part, int nparts, int M, int d, float eps, float* r,
+                         hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && nparts >= 1 && d >= 1 && eps >= 0.0f);
+  c.vec(part, true, false, M);
+  c.vec(r, true, false, M);
+  if (c.st != CODA_OK) return c.st;
+  if (M == 0) return CODA_OK;
+  if (coda_status s = device_ok()) return s;
+  hipLaunchKernelGGL(row_rms_kernel, dim3(cdiv(M, 256)), dim3(256), 0, stream, part, nparts, M,
+                     1.0f / (float)d, eps, r);
+  return launched();
+}
+
+coda_status coda_gemm_rowscale(const coda_bf16* A, int lda, const coda_bf16* W, int ldw,
+                               const float* r, coda_bf16* Y, int ldy, int M, int N, int K,
+                               hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && N >= 0 && K >= 0);
+  c.bmat(A, lda, K, true, M);
+  c.bmat(W, ldw, N);
+  c.vec(r, true, false, M);
+  c.bmat(Y, ldy, N, true, M);
+  c.shape(N % 8 == 0 && K % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (M == 0 || N == 0) return CODA_OK;
+  if (coda_status s = device_ok()) return s;
+  EpiLinear<true, false> e{r, nullptr, 0, Y, ldy};
+  return launch_gemm<false, true>(W, ldw, A, lda, N, M, K, e, stream);
+}
+
+static coda_status rope_common(const coda_bf16* A, int lda, const coda_bf16* W, int ldw,
+                               const float* r, const int32_t* pos, float theta, int head_dim,
+                               int n_rope, coda_bf16* Y, int ldy, int M, int N, int K, bool inv,
+                               hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && N >= 0 && K >= 0);
+  c.bmat(A, lda, K, true, M);
+  c.bmat(W, ldw, N);
+  c.vec(r, false, false, M);
+  c.vec(pos, true, false, M);
+  c.bmat(Y, ldy, N, true, M);
+  c.shape(N % 8 == 0 && K % 8 == 0);
+  c.unsupported(head_dim >= 2 && head_dim % 2 == 0 && n_rope >= 0 && n_rope <= N &&
+                n_rope % head_dim == 0 && n_rope % 8 == 0 && theta > 0.0f);
+  if (c.st != CODA_OK) return c.st;
+  if (M == 0 || N == 0) return CODA_OK;
+  if (coda_status s = device_ok()) return s;
+  const float l2t = (float)std::log2((double)theta);
+#define CODA_RP(HR, INV)                                                   \
+  {                                                                        \
+    EpiRope<HR, INV> e{r, pos, l2t, head_dim, n_rope, Y, ldy};             \
+    return launch_gemm<false, true>(W, ldw, A, lda, N, M, K, e, stream);   \
+  }
+  if (r && !inv) CODA_RP(true, false)
+  if (!r && !inv) CODA_RP(false, false)
+  if (r && inv) CODA_RP(true, true)
+  CODA_RP(false, true)
+#undef CODA_RP
+}
+
+coda_status coda_gemm_rope(const coda_bf16* A, int lda, const coda_bf16* W, int ldw,
+                           const float* r, const int32_t* pos, float theta, int head_dim,
+                           int n_rope, coda_bf16* Y, int ldy, int M, int N, int K,
+                           hipStream_t stream) {
+  return rope_common(A, lda, W, ldw, r, pos, theta, head_dim, n_rope, Y, ldy, M, N, K, false,
+                     stream);
+}
+
+coda_status coda_gemm_rope_bwd(const coda_bf16* A, int lda, const coda_bf16* W, int ldw,
+                               const float* r, const int32_t* pos, float theta, int head_dim,
+                               int n_rope, coda_bf16* Y, int ldy, int M, int N, int K,
+                               hipStream_t stream) {
+  return rope_common(A, lda, W, ldw, r, pos, theta, head_dim, n_rope, Y, ldy, M, N, K, true,
+                     stream);
+}
+
+coda_status coda_gemm_swiglu(const coda_bf16* A, int lda, const coda_bf16* Wgu, int ldw,
+                             const float* r, coda_bf16* Act, int ldact, coda_bf16* Pre, int ldp,
+                             int M, int F, int K, hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && F >= 0 && K >= 0);
+  c.shape(F <= (1 << 29));
+  if (c.st != CODA_OK) return c.st;
+  c.bmat(A, lda, K, true, M);
+  c.bmat(Wgu, ldw, 2 * F);
+  c.vec(r, false, false, M);
+  c.vec(Act, true, false, M);
+  if (c.st == CODA_OK && (ldact < F)) c.st = CODA_ERR_SHAPE;
+  if (c.st == CODA_OK && (!al16(Act) || ldact % 4 != 0)) c.st = CODA_ERR_ALIGN;
+  c.bmat(Pre, ldp, 2 * F, false, M);
+  c.shape(F % 4 == 0 && K % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (M == 0 || F == 0) return CODA_OK;
+  if (coda_status s = device_ok()) return s;
+#define CODA_SW(HR, HP)                                                          \
+  {                                                                              \
+    EpiSwiglu<HR, HP> e{r, Act, ldact, Pre, ldp};                                \
+    return launch_gemm<false, true>(Wgu, ldw, A, lda, 2 * F, M, K, e, stream);   \
+  }
+  if (r && Pre) CODA_SW(true, true)
+  if (r && !Pre) CODA_SW(true, false)
+  if (!r && Pre) CODA_SW(false, true)
+  CODA_SW(false, false)
+#undef CODA_SW
+}
+
+coda_status coda_lmhead_ce(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
+                           const int32_t* labels, float* lse, float* loss_row, float* loss_mean,
+                           void* ws, size_t ws_bytes, int M, int V, int d, hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && V >= 0 && d >= 0);
+  c.bmat(H, ldh, d, true, M);
+  c.bmat(W, ldw, V);
+  c.vec(labels, true, false, M);
+  c.vec(lse, true, false, M);
+  c.vec(loss_row, false);
+  c.vec(loss_mean, false);
+  c.shape(V % 8 == 0 && d % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (M == 0 || V == 0) return CODA_OK;
+  if (ws == nullptr || !al16(ws) || ws_bytes < coda_lmhead_ce_workspace(M, V))
+    return CODA_ERR_WORKSPACE;
+  if (coda_status s = device_ok()) return s;
+  const int np = coda_nparts(V);
+  float* pm = static_cast<float*>(ws);
+  float* ps = pm + (size_t)M * np;
+  float* tgt = ps + (size_t)M * np;
+  float* lrow = tgt + M;
+  if (loss_row == nullptr) loss_row = lrow;
+  EpiCE e{labels, pm, ps, tgt, np};
+  if (coda_status s = launch_gemm<false, true>(W, ldw, H, ldh, V, M, d, e, stream)) return s;
+  hipLaunchKernelGGL(ce_reduce_kernel, dim3(cdiv(M, 256)), dim3(256), 0, stream, pm, ps, tgt,
+                     labels, np, M, V, lse, loss_row);
+  if (coda_status s = launched()) return s;
+  if (loss_mean) {
+    hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, stream, loss_row, M, loss_mean);
+    return launched();
+  }
+  return CODA_OK;
+}
+
+coda_status coda_gemm_swiglu_bwd(const coda_bf16* dOut, int ldd, const coda_bf16* Wd, int ldw,
+                                 const coda_bf16* Pre, int ldp, coda_bf16* dPre, int lddp,
+                                 float* spart, int M, int F, int N, hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && F >= 0 && N >= 0 && F <= (1 << 29));
+  if (c.st != CODA_OK) return c.st;
+  c.bmat(dOut, ldd, N, true, M);
+  c.bmat(Wd, ldw, N);
+  c.bmat(Pre, ldp, 2 * F, true, M);
+  c.bmat(dPre, lddp, 2 * F, true, M);
+  c.vec(spart, false, false, M);
+  c.shape(F % 8 == 0 && N % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (M == 0 || F == 0) return CODA_OK;
+  if (coda_status s = device_ok()) return s;
+  const int np = coda_nparts(F);
+  // da[M x F] = dOut[M x N] Wd^T: features = F (rows of Wd, K-major), tokens = M.
+  if (spart) {
+    EpiSwigluBwd<true> e{Pre, ldp, dPre, lddp, spart, np};
+    return launch_gemm<true, true>(Wd, ldw, dOut, ldd, F, M, N, e, stream);
+  }
+  EpiSwigluBwd<false> e{Pre, ldp, dPre, lddp, nullptr, np};
+  return launch_gemm<true, true>(Wd, ldw, dOut, ldd, F, M, N, e, stream);
+}
+
+coda_status coda_row_rms_bwd(const float* spart, int nparts, int M, int d, float* s,
+                             hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && nparts >= 1 && d >= 1);
+  c.vec(spart, true, false, M);
+  c.vec(s, true, false, M);
+  if (c.st != CODA_OK) return c.st;
+  if (M == 0) return CODA_OK;
+  if (coda_status st = device_ok()) return st;
+  hipLaunchKernelGGL(row_sum_scale_kernel, dim3(cdiv(M, 256)), dim3(256), 0, stream, spart,
+                     nparts, M, 1.0f / (float)d, s);
+  return launched();
+}
+
+coda_status coda_gemm_rowscale_bwd(const coda_bf16* dY, int ldd, const coda_bf16* W1, int ldw,
+                                   const coda_bf16* U, int ldu, const coda_bf16* gamma,
+                                   const float* r, const float* s, const coda_bf16* dRes, int ldr,
+                                   coda_bf16* dU, int lddu, coda_bf16* N2, int ldn, float* gpart,
+                                   int M, int d, int N, hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && d >= 0 && N >= 0);
+  c.bmat(dY, ldd, N, true, M);
+  c.bmat(W1, ldw, N);
+  c.bmat(U, ldu, d, true, M);
+  c.vec(gamma, true, true);
+  c.vec(r, true, false, M);
+  c.vec(s, true, false, M);
+  c.bmat(dRes, ldr, d, false, M);
+  c.bmat(dU, lddu, d, true, M);
+  c.bmat(N2, ldn, d, false, M);
+  c.vec(gpart, false);
+  c.shape(d % 8 == 0 && N % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (M == 0 || d == 0) return CODA_OK;
+  if (coda_status st = device_ok()) return st;
+#define CODA_RB(HR, HN, HG)                                                             \
+  {                                                                                     \
+    EpiRowscaleBwd<HR, HN, HG> e{U, ldu, gamma, r, s, dRes, ldr, dU, lddu, N2, ldn,     \
+                                 gpart, d};                                             \
+    return launch_gemm<true, true, 256>(W1, ldw, dY, ldd, d, M, N, e, stream);          \
+  }
+  const bool hr = dRes != nullptr, hn = N2 != nullptr, hg = gpart != nullptr;
+  if (hr && hn && hg) CODA_RB(true, true, true)
+  if (hr && hn && !hg) CODA_RB(true, true, false)
+  if (hr && !hn && hg) CODA_RB(true, false, true)
+  if (hr && !hn && !hg) CODA_RB(true, false, false)
+  if (!hr && hn && hg) CODA_RB(false, true, true)
+  if (!hr && hn && !hg) CODA_RB(false, true, false)
+  if (!hr && !hn && hg) CODA_RB(false, false, true)
+  CODA_RB(false, false, false)
+#undef CODA_RB
+}
+
+coda_status coda_col_reduce(const float* gpart, int mparts, int d, float* dgamma,
+                            hipStream_t stream) {
+  Check c;
+  c.shape(mparts >= 1 && d >= 0);
+  c.vec(gpart);
+  c.vec(dgamma);
+  if (c.st != CODA_OK) return c.st;
+  if (d == 0) return CODA_OK;
+  if (coda_status st = device_ok()) return st;
+  hipLaunchKernelGGL(col_reduce_kernel, dim3(cdiv(d, 256)), dim3(256), 0, stream, gpart, mparts, d,
+                     dgamma);
+  return launched();
+}
+
+coda_status coda_gemm_wgrad(const coda_bf16* X, int ldx, const coda_bf16* dY, int ldd, float* dW,
+                            int lddw, int M, int K, int N, int accumulate, hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && K >= 0 && N >= 0);
+  c.bmat(X, ldx, K, true, M);
+  c.bmat(dY, ldd, N, true, M);
+  c.fmat(dW, lddw, N);
+  c.shape(K % 8 == 0 && N % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (K == 0 || N == 0) return CODA_OK;
+  if (coda_status st = device_ok()) return st;
+  // dW[K x N] = X^T dY: features = N (dY, contiguous along N -> MN-major),
+  // tokens = K (X, contiguous along K -> MN-major), reduction = M.
+  if (accumulate) {
+    EpiF32<true> e{dW, lddw};
+    return launch_gemm<false, false>(dY, ldd, X, ldx, N, K, M, e, stream);
+  }
+  EpiF32<false> e{dW, lddw};
+  return launch_gemm<false, false>(dY, ldd, X, ldx, N, K, M, e, stream);
+}
+
+coda_status coda_gemm_res_sumsq_bwd(const coda_bf16* dU, int ldu, const coda_bf16* W, int ldw,
+                                    const coda_bf16* X, int ldx, const coda_bf16* dRes, int ldr,
+                                    coda_bf16* dX, int lddx, float* dW, int lddw, int M, int N,
+                                    int K, hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && N >= 0 && K >= 0);
+  c.bmat(dU, ldu, N, true, M);
+  c.bmat(W, ldw, N);
+  c.bmat(dRes, ldr, K, false, M);
+  c.bmat(dX, lddx, K, true, M);
+  if (dW) {
+    c.bmat(X, ldx, K, true, M);
+    c.fmat(dW, lddw, N);
+  }
+  c.shape(N % 8 == 0 && K % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (M == 0 && dW == nullptr) return CODA_OK;
+  if (coda_status st = device_ok()) return st;
+  if (M > 0 && K > 0) {
+    // dX[M x K] = dU[M x N] W^T: features = K (rows of W, K-major over N).
+    coda_status s2;
+    if (dRes) {
+      EpiLinear<false, true> e{nullptr, dRes, ldr, dX, lddx};
+      s2 = launch_gemm<true, true>(W, ldw, dU, ldu, K, M, N, e, stream);
+    } else {
+      EpiLinear<false, false> e{nullptr, nullptr, 0, dX, lddx};
+      s2 = launch_gemm<true, true>(W, ldw, dU, ldu, K, M, N, e, stream);
+    }
+    if (s2 != CODA_OK) return s2;
+  }
+  if (dW) return coda_gemm_wgrad(X, ldx, dU, ldu, dW, lddw, M, K, N, 0, stream);
+  return CODA_OK;
+}
+
+coda_status coda_lmhead_ce_bwd(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
+                               const int32_t* labels, const float* lse, float grad_scale,
+                               coda_bf16* dH, int lddh, float* dW, int lddw, void* ws,
+                               size_t ws_bytes, int M, int V, int d, hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && V >= 0 && d >= 0);
+  c.bmat(H, ldh, d, true, M);
+  c.bmat(W, ldw, V);
+  c.vec(labels, true, false, M);
+  c.vec(lse, true, false, M);
+  c.bmat(dH, lddh, d, true, M);
+  c.fmat(dW, lddw, V);
+  c.shape(V % 8 == 0 && d % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (V == 0 || d == 0) return CODA_OK;
+  if (M > 0 && (ws == nullptr || !al16(ws) || ws_bytes < coda_lmhead_ce_bwd_workspace(M, V, d)))
+    return CODA_ERR_WORKSPACE;
+  if (coda_status st = device_ok()) return st;
+  if (M == 0)  // no rows: dW = H^T D over an empty reduction = 0
+    return coda_gemm_wgrad(H, ldh, nullptr, V, dW, lddw, 0, d, V, 0, stream);
+  // Rows per chunk: as many as the workspace holds, a multiple of 256.
+  size_t rows = ws_bytes / ((size_t)V * 2);
+  if (rows >= (size_t)M) rows = (size_t)M;
+  else rows = (rows / 256) * 256;
+  if (rows == 0) rows = (size_t)M;  // M < 256 and the workspace holds all rows
+  uint16_t* D = static_cast<uint16_t*>(ws);
+  for (int m0 = 0; m0 < M; m0 += (int)rows) {
+    const int mc = (M - m0) < (int)rows ? (M - m0) : (int)rows;
+    const uint16_t* Hc = H + (size_t)m0 * ldh;
+    // 1) recompute logits and form dlogits D[mc x V] (bf16) in the epilogue
+    EpiCEBwd e1{labels + m0, lse + m0, grad_scale, D, V};
+    if (coda_status s = launch_gemm<false, true>(W, ldw, Hc, ldh, V, mc, d, e1, stream)) return s;
+    // 2) dH[mc x d] = D W^T: features = d (rows of W, contiguous along V)
+    EpiLinear<false, false> e2{nullptr, nullptr, 0, dH + (size_t)m0 * lddh, lddh};
+    if (coda_status s = launch_gemm<true, true>(W, ldw, D, V, d, mc, V, e2, stream)) return s;
+    // 3) dW[d x V] (+)= Hc^T D
+    if (coda_status s = coda_gemm_wgrad(Hc, ldh, D, V, dW, lddw, mc, d, V, m0 > 0, stream))
+      return s;
+  }
+  return CODA_OK;
+}
+
+}  // extern "C"

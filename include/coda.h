@@ -1,0 +1,219 @@
+/*
+ * coda.h - C ABI of the MI355X (gfx950) CODA GEMM-epilogue library, libcoda.so.
+ *
+ * Each fused call is one bf16 MFMA GEMM whose epilogue performs the
+ * non-attention Transformer-block work on the output tile while it is still in
+ * registers, before the global store, as described in "CODA: Rewriting
+ * Transformer Blocks as GEMM-Epilogue Programs" (abstract; Figure 3) and in
+ * the reading notes "CODA GEMM-Epilogue Programming" (section 1, "The Epilogue
+ * Concept").  The auxiliary reductions are small bandwidth kernels.
+ *
+ * Conventions (every entry point):
+ *  - Matrices are row-major with a leading dimension ld* in elements.
+ *    Weights are stored [in x out] (K x N), so a forward projection is X W.
+ *  - bf16 is bfloat16 bits (coda_bf16); the GEMM accumulates in fp32 and
+ *    rounds its bf16 outputs to nearest-even.  Row/column statistics,
+ *    losses and weight gradients are fp32.
+ *  - All pointers are DEVICE pointers owned by the caller.  The library never
+ *    allocates, frees or synchronises, and keeps no mutable global state;
+ *    calls are asynchronous and ordered on `stream` (NULL = default stream).
+ *  - Requirements: bf16 base pointers 16-byte aligned and bf16 ld % 8 == 0;
+ *    fp32 matrix pointers 16-byte aligned and fp32 ld % 4 == 0; every output
+ *    width (N, F, d, V) % 8 == 0; the reduction length K % 8 == 0 when the
+ *    operand is contiguous along K (every forward and data-gradient call).
+ *    The token count M is arbitrary; ragged edge tiles are masked.
+ *  - Errors: validation happens before any launch and returns a status
+ *    without touching the device.  CODA_ERR_HIP reports a launch error
+ *    (hipGetLastError); device faults surface at the caller's next sync.
+ *    Optional outputs ("opt") are skipped when NULL.
+ *  - Outputs must not alias inputs unless stated.  Results are deterministic:
+ *    no atomics, fixed reduction order.
+ */
+#ifndef CODA_H_
+#define CODA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t coda_bf16;
+
+typedef enum coda_status {
+  CODA_OK = 0,
+  CODA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  CODA_ERR_SHAPE = 2,       /* a size or leading dimension is invalid         */
+  CODA_ERR_ALIGN = 3,       /* a pointer or leading dimension is misaligned   */
+  CODA_ERR_UNSUPPORTED = 4, /* device is not gfx950, or an untiled constraint */
+  CODA_ERR_HIP = 5,         /* the HIP runtime reported an error              */
+  CODA_ERR_WORKSPACE = 6    /* workspace missing or too small                 */
+} coda_status;
+
+/* Human-readable text of a status code (static storage). */
+const char* coda_status_str(coda_status s);
+
+/* Library version string, e.g. "coda-gfx950 0.1". */
+const char* coda_version(void);
+
+/* Number of per-row partial columns a fused call writes for an output of
+ * width N (one per 128-wide wavefront output tile): ceil(N / 128). */
+int coda_nparts(int N);
+
+/* Number of per-column partial rows written by coda_gemm_rowscale_bwd for M
+ * tokens (one per 128-token wavefront output tile): ceil(M / 128). */
+int coda_mparts(int M);
+
+/* Workspace bytes coda_lmhead_ce needs for M rows and vocabulary V. */
+size_t coda_lmhead_ce_workspace(int M, int V);
+
+/* Minimal workspace bytes coda_lmhead_ce_bwd needs (one 256-row chunk of
+ * bf16 dlogits); a larger workspace processes more rows per chunk, up to
+ * M * V * 2 bytes (no chunking). */
+size_t coda_lmhead_ce_bwd_workspace(int M, int V, int d);
+
+/* ---------------------------------------------------------------------------
+ * Plain GEMM, store-only epilogue: Y[M x N] = bf16(X[M x K] W[K x N]).
+ * The "fixed mainloop" every fused call shares; also the unfused baseline.
+ * ------------------------------------------------------------------------- */
+coda_status coda_gemm(const coda_bf16* X, int ldx, const coda_bf16* W, int ldw,
+                      coda_bf16* Y, int ldy, int M, int N, int K, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Forward
+ * ------------------------------------------------------------------------- */
+
+/* GEMM1 of GEMM -> residual -> RMSNorm -> GEMM (reading notes section 2;
+ * paper Figure 4 and Listing 2):
+ *   u = X W + Z                       -> U  (bf16, M x N)
+ *   h2 = u * gamma (per column)       -> H2 (bf16, opt; needs gamma)
+ *   part[i, p] = sum_{j in part p} u_ij^2 of the UNSCALED fp32 u
+ *                                     -> part (fp32, opt, M x coda_nparts(N),
+ *                                        row stride coda_nparts(N))
+ * Z may be NULL (no residual).  With gamma, H2 and part all NULL this is a
+ * GEMM plus residual add (e.g. an MLP down projection). */
+coda_status coda_gemm_res_sumsq(const coda_bf16* X, int ldx, const coda_bf16* W, int ldw,
+                                const coda_bf16* Z, int ldz, const coda_bf16* gamma,
+                                coda_bf16* U, int ldu, coda_bf16* H2, int ldh, float* part,
+                                int M, int N, int K, hipStream_t stream);
+
+/* Auxiliary reduction (paper Figure 4 / Figure 5 caption):
+ *   r_i = 1 / sqrt( sum_p part[i, p] / d + eps )
+ * part is fp32 [M x nparts] (row stride nparts), r is fp32 [M]. */
+coda_status coda_row_rms(const float* part, int nparts, int M, int d, float eps, float* r,
+                         hipStream_t stream);
+
+/* GEMM2 with the delayed RMSNorm row scale (reading notes section 2):
+ *   Y = bf16( r_i * (A W)_ij ),  A = h2 [M x K], W [K x N], r fp32 [M]. */
+coda_status coda_gemm_rowscale(const coda_bf16* A, int lda, const coda_bf16* W, int ldw,
+                               const float* r, coda_bf16* Y, int ldy, int M, int N, int K,
+                               hipStream_t stream);
+
+/* GEMM + RoPE pair map (paper Figure 7; RoFormer rotation):
+ *   t = r_i * (A W)_ij  (r opt: NULL means 1)
+ *   for each even column c < n_rope, k = (c mod head_dim) / 2,
+ *   ang = pos_i * theta^(-2k / head_dim):
+ *     (y_c, y_c+1) = (t_c cos - t_c+1 sin, t_c sin + t_c+1 cos)
+ *   columns >= n_rope pass through.  pos is int32 [M].
+ * Needs head_dim even, n_rope % head_dim == 0 and n_rope <= N. */
+coda_status coda_gemm_rope(const coda_bf16* A, int lda, const coda_bf16* W, int ldw,
+                           const float* r, const int32_t* pos, float theta, int head_dim,
+                           int n_rope, coda_bf16* Y, int ldy, int M, int N, int K,
+                           hipStream_t stream);
+
+/* GEMM + SwiGLU pair map (paper Figure 7; reading notes section 2):
+ *   (g, v) = r_i * ((A Wgu)_i,2j , (A Wgu)_i,2j+1)   (r opt)
+ *   Act_ij = g * sigmoid(g) * v         -> Act (bf16, M x F)
+ *   Pre = bf16(g, v) interleaved        -> Pre (bf16, opt, M x 2F)
+ * Wgu is [K x 2F] with gate columns even and up columns odd. */
+coda_status coda_gemm_swiglu(const coda_bf16* A, int lda, const coda_bf16* Wgu, int ldw,
+                             const float* r, coda_bf16* Act, int ldact, coda_bf16* Pre,
+                             int ldp, int M, int F, int K, hipStream_t stream);
+
+/* LM head + cross-entropy (reading notes section 2, "Cross-entropy loss"):
+ * logits l = H W (fp32, never stored); the GEMM epilogue writes per-tile
+ * (max, sum exp) and gathers the target logit; an auxiliary kernel forms
+ *   lse_i = log sum_k exp(l_ik),  loss_row_i = lse_i - l_{i,label_i},
+ *   loss_mean = sum_i loss_row_i / M  (fixed order).
+ * A label outside [0, V) gives a NaN row loss.  H [M x d], W [d x V],
+ * labels int32 [M]; lse, loss_row fp32 [M] (loss_row opt), loss_mean fp32 [1]
+ * (opt); ws >= coda_lmhead_ce_workspace(M, V) bytes, 16-byte aligned. */
+coda_status coda_lmhead_ce(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
+                           const int32_t* labels, float* lse, float* loss_row, float* loss_mean,
+                           void* ws, size_t ws_bytes, int M, int V, int d, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Backward ("reverse fusion", reading notes section 3; paper Figure 9)
+ * ------------------------------------------------------------------------- */
+
+/* Data-gradient GEMM with the SwiGLU backward pair map (1 -> 2):
+ *   da = dOut Wd^T   (dOut [M x N], Wd [F x N] used transposed)
+ *   with (g, v) = Pre_i,2j , Pre_i,2j+1 and s = sigmoid(g):
+ *   dPre_i,2j = da v s (1 + g (1 - s)),  dPre_i,2j+1 = da g s
+ *   spart[i, p] = sum_{j in part p} (dPre_2j g + dPre_2j+1 v)  (fp32, opt,
+ *   M x coda_nparts(F)): the partial of sumcols(dY * y) that the RMSNorm
+ *   backward statistic s needs (reading notes section 3). */
+coda_status coda_gemm_swiglu_bwd(const coda_bf16* dOut, int ldd, const coda_bf16* Wd, int ldw,
+                                 const coda_bf16* Pre, int ldp, coda_bf16* dPre, int lddp,
+                                 float* spart, int M, int F, int N, hipStream_t stream);
+
+/* Auxiliary reduction of the RMSNorm backward statistic (reading notes
+ * section 3): s_i = sum_p spart[i, p] / d, d = the RMSNorm width. */
+coda_status coda_row_rms_bwd(const float* spart, int nparts, int M, int d, float* s,
+                             hipStream_t stream);
+
+/* Data-gradient GEMM with the RMSNorm backward epilogue:
+ *   G = dY W1^T   (dY [M x N], W1 [d x N] used transposed)
+ *   dU = dRes + r_i (G * gamma) - r_i^2 s_i u          (bf16, M x d)
+ *   N2 = bf16(r_i u * gamma)  (opt; the weight-gradient operand)
+ *   gpart[q, j] = sum_{i in token part q} r_i G_ij u_ij (fp32, opt,
+ *   coda_mparts(M) x d): the column partials of dgamma.
+ * U is the RMSNorm input [M x d]; r, s fp32 [M]; dRes opt. */
+coda_status coda_gemm_rowscale_bwd(const coda_bf16* dY, int ldd, const coda_bf16* W1, int ldw,
+                                   const coda_bf16* U, int ldu, const coda_bf16* gamma,
+                                   const float* r, const float* s, const coda_bf16* dRes, int ldr,
+                                   coda_bf16* dU, int lddu, coda_bf16* N2, int ldn, float* gpart,
+                                   int M, int d, int N, hipStream_t stream);
+
+/* Column reduction of the dgamma partials: dgamma_j = sum_q gpart[q, j]. */
+coda_status coda_col_reduce(const float* gpart, int mparts, int d, float* dgamma,
+                            hipStream_t stream);
+
+/* RoPE backward epilogue: same arguments as coda_gemm_rope; applies the
+ * inverse rotation (ang -> -ang) after the optional row scale. */
+coda_status coda_gemm_rope_bwd(const coda_bf16* A, int lda, const coda_bf16* W, int ldw,
+                               const float* r, const int32_t* pos, float theta, int head_dim,
+                               int n_rope, coda_bf16* Y, int ldy, int M, int N, int K,
+                               hipStream_t stream);
+
+/* Backward of u = X W + Z:
+ *   dX = dU W^T (+ dRes)   (bf16, M x K)       W [K x N] used transposed
+ *   dW = X^T dU            (fp32, opt, K x N)  */
+coda_status coda_gemm_res_sumsq_bwd(const coda_bf16* dU, int ldu, const coda_bf16* W, int ldw,
+                                    const coda_bf16* X, int ldx, const coda_bf16* dRes, int ldr,
+                                    coda_bf16* dX, int lddx, float* dW, int lddw,
+                                    int M, int N, int K, hipStream_t stream);
+
+/* Weight gradient: dW[K x N] = X^T dY (fp32); accumulate != 0 adds into dW.
+ * X [M x K], dY [M x N]; M (the reduction) is arbitrary. */
+coda_status coda_gemm_wgrad(const coda_bf16* X, int ldx, const coda_bf16* dY, int ldd,
+                            float* dW, int lddw, int M, int K, int N, int accumulate,
+                            hipStream_t stream);
+
+/* LM head + cross-entropy backward of loss = grad_scale * sum_i loss_row_i
+ * (grad_scale = 1/M for the mean):
+ *   recompute l = H W; dlogits D = (exp(l - lse_i) - [k == label_i]) grad_scale
+ *   (bf16, in ws, row chunks); dH = D W^T (bf16, M x d); dW = H^T D (fp32, d x V).
+ * lse comes from coda_lmhead_ce.  ws >= coda_lmhead_ce_bwd_workspace(M,V,d). */
+coda_status coda_lmhead_ce_bwd(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
+                               const int32_t* labels, const float* lse, float grad_scale,
+                               coda_bf16* dH, int lddh, float* dW, int lddw, void* ws,
+                               size_t ws_bytes, int M, int V, int d, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CODA_H_ */

@@ -1,0 +1,99 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/coda.h declares, and rejects bad arguments before any device call."""
+
+import ctypes
+import os
+
+import pytest
+
+from gemm_epilogue_transformer_mainloop_amd import coda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(coda.LIB_PATH):
+        from gemm_epilogue_transformer_mainloop_amd import build
+
+        build.build()
+    return coda.lib()
+
+
+def test_exports_every_header_function(L):
+    names = coda.header_functions()
+    assert len(names) >= 20
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    # the binding covers the whole header
+    assert set(names) == set(coda._SIGS), set(names) ^ set(coda._SIGS)
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert coda.status_str(s)
+    assert coda.status_str(0) == "ok"
+    assert L.coda_version().decode().startswith("coda-gfx950")
+
+
+def test_queries(L):
+    assert coda.coda_nparts(2048) == 16
+    assert coda.coda_nparts(1) == 1
+    assert coda.coda_nparts(128256) == 1002
+    assert coda.coda_nparts(0) == 0
+    assert coda.coda_mparts(8192) == 64
+    assert coda.coda_mparts(129) == 2
+    M, V = 8192, 128256
+    assert coda.coda_lmhead_ce_workspace(M, V) == (2 * M * 1002 + 2 * M) * 4
+    assert coda.coda_lmhead_ce_bwd_workspace(M, V, 2048) == 256 * V * 2
+    assert coda.coda_lmhead_ce_bwd_workspace(100, V, 2048) == 100 * V * 2
+
+
+# Fake, 256-byte aligned, never dereferenced: every call below fails validation first.
+A16 = ctypes.c_void_p(0x100000)
+A16b = ctypes.c_void_p(0x200000)
+A16c = ctypes.c_void_p(0x300000)
+MIS = ctypes.c_void_p(0x100002)
+
+
+def test_gemm_validation(L):
+    f = L.coda_gemm
+    assert f(None, 64, A16, 64, A16b, 64, 16, 64, 64, None) == 1               # NULL X
+    assert f(A16, 64, A16b, 64, A16c, 64, -1, 64, 64, None) == 2               # M < 0
+    assert f(A16, 32, A16b, 64, A16c, 64, 16, 64, 64, None) == 2               # ldx < K
+    assert f(A16, 64, A16b, 64, A16c, 64, 16, 60, 64, None) == 2               # N % 8
+    assert f(MIS, 64, A16b, 64, A16c, 64, 16, 64, 64, None) == 3               # misaligned
+    assert f(A16, 68, A16b, 64, A16c, 64, 16, 64, 64, None) == 3               # ld % 8
+    assert f(A16, 64, A16b, 64, A16c, 64, 0, 64, 64, None) == 0                # empty M: no-op
+
+
+def test_fused_validation(L):
+    # res_sumsq: H2 without gamma
+    assert L.coda_gemm_res_sumsq(A16, 64, A16b, 64, None, 0, None, A16c, 64, A16, 64, None,
+                                 16, 64, 64, None) == 1
+    # row_rms: nparts < 1
+    assert L.coda_row_rms(A16, 0, 16, 64, ctypes.c_float(1e-6), A16b, None) == 2
+    # rope: n_rope not a multiple of head_dim
+    assert L.coda_gemm_rope(A16, 64, A16b, 128, None, A16c, ctypes.c_float(1e4), 64, 96, A16, 128,
+                            16, 128, 64, None) == 4
+    # rope: odd head_dim
+    assert L.coda_gemm_rope(A16, 64, A16b, 128, None, A16c, ctypes.c_float(1e4), 63, 0, A16, 128,
+                            16, 128, 64, None) == 4
+    # swiglu: NULL act
+    assert L.coda_gemm_swiglu(A16, 64, A16b, 64, None, None, 64, None, 0, 16, 32, 64, None) == 1
+    # lmhead: workspace too small
+    assert L.coda_lmhead_ce(A16, 64, A16b, 128, A16c, A16, None, None, A16b, 16, 16, 128, 64,
+                            None) == 6
+    # swiglu_bwd: ldp < 2F
+    assert L.coda_gemm_swiglu_bwd(A16, 64, A16b, 64, A16c, 64, A16, 128, None, 16, 64, 64,
+                                  None) == 2
+    # rowscale_bwd: NULL s
+    assert L.coda_gemm_rowscale_bwd(A16, 64, A16b, 64, A16c, 64, A16, A16b, None, None, 0, A16c,
+                                    64, None, 0, None, 16, 64, 64, None) == 1
+    # wgrad: misaligned fp32 ld
+    assert L.coda_gemm_wgrad(A16, 64, A16b, 64, A16c, 66, 16, 64, 64, 0, None) == 3
+    # lmhead bwd: no workspace
+    assert L.coda_lmhead_ce_bwd(A16, 64, A16b, 128, A16c, A16, ctypes.c_float(1.0), A16b, 64, A16c,
+                                128, None, 0, 16, 128, 64, None) == 6
+    # col_reduce: mparts < 1
+    assert L.coda_col_reduce(A16, 0, 64, A16b, None) == 2
