@@ -1,0 +1,407 @@
+#!/usr/bin/env python3
+"""Benchmark of the CODA GEMM-epilogue path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--out FILE]
+
+One step = one pass of the fused GEMM -> residual -> RMSNorm -> GEMM forward
+at the Llama-3-1B-like shape (M = 8192 tokens, d = 2048) on seeded synthetic
+bf16 inputs already resident in HBM:
+
+  coda_gemm_res_sumsq  u = x W0 + z, h2 = u*gamma, sum-of-squares partials  (8192 x 2048 x 2048)
+  coda_row_rms         r = 1/sqrt(sum/d + eps)                             (aux, 8192 x 16)
+  coda_gemm_rowscale   y = r * (h2 W1)                                     (8192 x 2048 x 2048)
+  coda_gemm_rope       y_qkv = rope(r * (h2 W1qkv)), Q and K rotated        (8192 x 3072 x 2048)
+
+The metric counts only the GEMMs' algorithmic 2*M*N*K FLOPs.  Each kernel is
+timed with HIP events recorded on the stream it is launched on, inside the
+timed region.  Rank 0 prints ONE JSON line on stdout; tables go to stderr.
+``--all`` also measures every fused call of the five synthetic workloads
+against the plain GEMM of the same shape and writes them to ``--out``.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "fused GEMM+epilogue TFLOP/s and % of bf16 MFMA peak (1 MI355X)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gemm_epilogue_transformer_mainloop_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------
+# timing helpers
+# ----------------------------------------------------------------------------
+
+
+class OpTimer:
+    """Per-op HIP event pairs recorded on the current stream, averaged after sync."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.ev = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        s = t.cuda.Event(enable_timing=True)
+        e = t.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.ev.setdefault(name, []).append((s, e))
+        return out
+
+    def mean_ms(self):
+        return {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in self.ev.items()}
+
+
+def time_fn(torch, fn, iters=20, warmup=5):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(iters):
+        s.record()
+        fn()
+        e.record()
+        e.synchronize()
+        times.append(s.elapsed_time(e))
+    return float(np.median(times)), float(np.min(times))
+
+
+# ----------------------------------------------------------------------------
+# config-2 step
+# ----------------------------------------------------------------------------
+
+
+def c2_inputs(torch, synth):
+    c = synth.CONFIGS[2]
+    M, d, K, N, NR = c["M"], c["d"], c["K"], c["N"], c["n_rope_cols"]
+    p = synth.norm_block_inputs(2, M, d, K, N, n_rope_cols=NR)
+    T = {k: v.torch("cuda") for k, v in p.items() if hasattr(v, "bits")}
+    T["pos"] = torch.from_numpy(p["pos"]).cuda()
+    return p, T, (M, d, K, N, NR)
+
+
+def c2_flops(M, d, K, N, NR):
+    return {"res_sumsq": 2.0 * M * d * K, "rowscale": 2.0 * M * N * d, "rope": 2.0 * M * NR * d}
+
+
+def make_c2_step(torch, coda, T, dims, eps):
+    M, d, K, N, NR = dims
+    n_rope = 2560  # Q (32 heads) and K (8 heads) of the 2048:512:512 QKV split; V passes through
+    bf = torch.bfloat16
+    buf = {
+        "U": torch.empty(M, d, dtype=bf, device="cuda"),
+        "H2": torch.empty(M, d, dtype=bf, device="cuda"),
+        "part": torch.empty(M, coda.coda_nparts(d), dtype=torch.float32, device="cuda"),
+        "r": torch.empty(M, dtype=torch.float32, device="cuda"),
+        "Y": torch.empty(M, N, dtype=bf, device="cuda"),
+        "Yr": torch.empty(M, NR, dtype=bf, device="cuda"),
+    }
+
+    def step(tm=None):
+        run = tm.run if tm is not None else (lambda n, f: f())
+        run("res_sumsq", lambda: coda.coda_gemm_res_sumsq(T["x"], T["W0"], T["z"], T["gamma"], U=buf["U"],
+                                                           H2=buf["H2"], part=buf["part"]))
+        run("row_rms", lambda: coda.coda_row_rms(buf["part"], d, eps, r=buf["r"]))
+        run("rowscale", lambda: coda.coda_gemm_rowscale(buf["H2"], T["W1"], buf["r"], Y=buf["Y"]))
+        run("rope", lambda: coda.coda_gemm_rope(buf["H2"], T["W1r"], buf["r"], T["pos"], 500000.0, 64, n_rope,
+                                                 Y=buf["Yr"]))
+
+    return step, buf, n_rope
+
+
+def cpu_baseline(p, dims, n_rope, min_seconds=10.0, max_steps=20):
+    """The fp64 oracle timed on the host on whole config-2 steps (at least min_seconds)."""
+    from oracle import coda_oracle as O
+    from threadpoolctl import threadpool_info
+
+    M, d, K, N, NR = dims
+    x, W0, z, g, W1, W1r = (p[k].f64() for k in ("x", "W0", "z", "gamma", "W1", "W1r"))
+    pos = p["pos"]
+    flops = sum(c2_flops(*dims).values())
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        u, h2, ss = O.res_sumsq(x, W0, z, g)
+        n2, r = O.rmsnorm(u, g, p["eps"])
+        y = O.gemm(n2, W1)
+        yr = O.rope(O.gemm(n2, W1r), pos, 500000.0, 64, n_rope)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or steps >= max_steps:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(flops * steps / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{steps} whole config-2 steps (M=8192, d=2048; 240.5 GFLOP each) in fp64 numpy, "
+                      f"{el:.1f} s"}
+
+
+def load_traffic(kernel_key):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    ent = t.get(kernel_key)
+    if not ent or ent.get("src_hash") != src_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+# --all: every fused call of the five workloads vs the plain GEMM of the same shape
+# ----------------------------------------------------------------------------
+
+
+def bench_all(torch, coda, synth, iters=20):
+    bf = torch.bfloat16
+    rows = []
+
+    def rnd(*shape, std=1.0):
+        return (torch.randn(*shape, device="cuda") * std).to(bf)
+
+    def rec(cfg, op, M, N, K, fn, plain=None, aux_bytes=None):
+        med, mn = time_fn(torch, fn, iters)
+        ent = {"config": cfg, "op": op, "M": M, "N": N, "K": K, "us_median": med * 1e3, "us_min": mn * 1e3}
+        if K:
+            tf = 2.0 * M * N * K / (med * 1e-3) / 1e12
+            ent.update(tflops=tf, pct_peak=100 * tf / PEAK_BF16_TFLOPS)
+        if aux_bytes:
+            ent.update(gbs=aux_bytes / (med * 1e-3) / 1e9, pct_hbm=100 * aux_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS)
+        if plain is not None:
+            pm, _ = time_fn(torch, plain, iters)
+            ent.update(plain_us=pm * 1e3, ratio_to_plain=med / pm)
+        rows.append(ent)
+        log(json.dumps(ent))
+
+    def plain_nn(M, N, K):
+        X, W, Y = rnd(M, K), rnd(K, N), torch.empty(M, N, dtype=bf, device="cuda")
+        return lambda: coda.coda_gemm(X, W, Y)
+
+    def plain_nt(M, N, K):  # Y[M,N] = A[M,K] B[N,K]^T
+        A, B, Y = rnd(M, K), rnd(N, K), torch.empty(M, N, dtype=bf, device="cuda")
+        return lambda: coda.coda_gemm_res_sumsq_bwd(A, B, dX=Y, want_dw=False)
+
+    for cfg, (M, d, K, N) in {1: (256, 512, 512, 1024), 2: (8192, 2048, 2048, 2048)}.items():
+        x, W0, z, g = rnd(M, K), rnd(K, d, std=K ** -0.5), rnd(M, d), torch.ones(d, dtype=bf, device="cuda")
+        U, H2 = torch.empty(M, d, dtype=bf, device="cuda"), torch.empty(M, d, dtype=bf, device="cuda")
+        part = torch.empty(M, coda.coda_nparts(d), device="cuda")
+        rec(cfg, "res_sumsq", M, d, K, lambda: coda.coda_gemm_res_sumsq(x, W0, z, g, U, H2, part), plain_nn(M, d, K))
+        r = torch.empty(M, device="cuda")
+        rec(cfg, "row_rms", M, 0, 0, lambda: coda.coda_row_rms(part, d, 1e-6, r), aux_bytes=M * part.shape[1] * 4 + M * 4)
+        W1, Y = rnd(d, N, std=d ** -0.5), torch.empty(M, N, dtype=bf, device="cuda")
+        rec(cfg, "rowscale", M, N, d, lambda: coda.coda_gemm_rowscale(H2, W1, r, Y), plain_nn(M, N, d))
+        if cfg == 2:
+            W1r, Yr = rnd(d, 3072, std=d ** -0.5), torch.empty(M, 3072, dtype=bf, device="cuda")
+            pos = torch.arange(M, device="cuda", dtype=torch.int32) % 2048
+            rec(cfg, "rope", M, 3072, d, lambda: coda.coda_gemm_rope(H2, W1r, r, pos, 5e5, 64, 2560, Yr),
+                plain_nn(M, 3072, d))
+    # config 3: SwiGLU MLP fwd + bwd
+    M, d, F = 8192, 2048, 8192
+    x, Wgu, Wd, dY = rnd(M, d), rnd(d, 2 * F, std=d ** -0.5), rnd(F, d, std=F ** -0.5), rnd(M, d)
+    act, pre = torch.empty(M, F, dtype=bf, device="cuda"), torch.empty(M, 2 * F, dtype=bf, device="cuda")
+    rec(3, "swiglu", M, 2 * F, d, lambda: coda.coda_gemm_swiglu(x, Wgu, None, act, pre), plain_nn(M, 2 * F, d))
+    out = torch.empty(M, d, dtype=bf, device="cuda")
+    rec(3, "down+residual", M, d, F, lambda: coda.coda_gemm_res_sumsq(act, Wd, x, U=out, want_part=False),
+        plain_nn(M, d, F))
+    dpre = torch.empty(M, 2 * F, dtype=bf, device="cuda")
+    rec(3, "swiglu_bwd", M, F, d, lambda: coda.coda_gemm_swiglu_bwd(dY, Wd, pre, dpre, want_spart=False),
+        plain_nt(M, F, d))
+    dX = torch.empty(M, d, dtype=bf, device="cuda")
+    rec(3, "dgrad+residual", M, d, 2 * F, lambda: coda.coda_gemm_res_sumsq_bwd(dpre, Wgu, dRes=dY, dX=dX, want_dw=False),
+        plain_nt(M, d, 2 * F))
+    dWgu = torch.empty(d, 2 * F, device="cuda")
+    rec(3, "wgrad dWgu", d, 2 * F, M, lambda: coda.coda_gemm_wgrad(x, dpre, dWgu))
+    dWd = torch.empty(F, d, device="cuda")
+    rec(3, "wgrad dWd", F, d, M, lambda: coda.coda_gemm_wgrad(act, dY, dWd))
+    del x, Wgu, Wd, dY, act, pre, dpre, dX, dWgu, dWd, out
+    # config 4: LM head + CE
+    M, d, V = 8192, 2048, 128256
+    h, W = rnd(M, d), rnd(d, V, std=d ** -0.5)
+    labels = torch.randint(0, V, (M,), device="cuda", dtype=torch.int32)
+    ws = torch.empty(coda.coda_lmhead_ce_workspace(M, V), dtype=torch.uint8, device="cuda")
+    lse, lr, lm = (torch.empty(M, device="cuda"), torch.empty(M, device="cuda"), torch.empty(1, device="cuda"))
+    rec(4, "lmhead_ce", M, V, d, lambda: coda.coda_lmhead_ce(h, W, labels, lse, lr, lm, ws), plain_nn(M, V, d))
+    dH, dW = torch.empty(M, d, dtype=bf, device="cuda"), torch.empty(d, V, device="cuda")
+    wsb = torch.empty(M * V * 2, dtype=torch.uint8, device="cuda")
+    med, mn = time_fn(torch, lambda: coda.coda_lmhead_ce_bwd(h, W, labels, lse, 1.0 / M, dH, dW, wsb), 5, 2)
+    ent = {"config": 4, "op": "lmhead_ce_bwd (3 GEMMs)", "M": M, "N": V, "K": d, "us_median": med * 1e3,
+           "tflops": 3 * 2.0 * M * V * d / (med * 1e-3) / 1e12}
+    ent["pct_peak"] = 100 * ent["tflops"] / PEAK_BF16_TFLOPS
+    rows.append(ent)
+    log(json.dumps(ent))
+    del h, W, ws, wsb, dH, dW
+    # config 5: the block-backward fused calls at 8B-like shape
+    M, d, F = 8192, 4096, 14336
+    dOut, Wd, Wgu = rnd(M, d), rnd(F, d, std=F ** -0.5), rnd(d, 2 * F, std=d ** -0.5)
+    pre, dpre = rnd(M, 2 * F), torch.empty(M, 2 * F, dtype=bf, device="cuda")
+    spart = torch.empty(M, coda.coda_nparts(F), device="cuda")
+    rec(5, "swiglu_bwd+s", M, F, d, lambda: coda.coda_gemm_swiglu_bwd(dOut, Wd, pre, dpre, spart), plain_nt(M, F, d))
+    s = torch.empty(M, device="cuda")
+    rec(5, "row_rms_bwd", M, 0, 0, lambda: coda.coda_row_rms_bwd(spart, d, s), aux_bytes=spart.numel() * 4 + M * 4)
+    u, gam, r = rnd(M, d), torch.ones(d, dtype=bf, device="cuda"), torch.ones(M, device="cuda")
+    dU, N2 = torch.empty(M, d, dtype=bf, device="cuda"), torch.empty(M, d, dtype=bf, device="cuda")
+    gpart = torch.empty(coda.coda_mparts(M), d, device="cuda")
+    rec(5, "rowscale_bwd", M, d, 2 * F, lambda: coda.coda_gemm_rowscale_bwd(dpre, Wgu, u, gam, r, s, dOut, dU, N2, gpart),
+        plain_nt(M, d, 2 * F))
+    dg = torch.empty(d, device="cuda")
+    rec(5, "col_reduce", 0, d, 0, lambda: coda.coda_col_reduce(gpart, dg), aux_bytes=gpart.numel() * 4 + d * 4)
+    dW = torch.empty(d, 2 * F, device="cuda")
+    rec(5, "wgrad dWgu", d, 2 * F, M, lambda: coda.coda_gemm_wgrad(N2, dpre, dW))
+    return rows
+
+
+# ----------------------------------------------------------------------------
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--all", action="store_true", help="also time every fused call of the five workloads")
+    ap.add_argument("--out", default=None, help="file for the --all table (JSON lines)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; --gpus must be 1 (no multi-GPU path is built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gemm_epilogue_transformer_mainloop_amd import coda, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    coda.lib()  # fails loudly if the HIP library is not built
+
+    if args.copy_calib:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x {n} bytes read + {n} bytes written")
+        return
+
+    p, T, dims = c2_inputs(torch, synth)
+    M, d, K, N, NR = dims
+    step, buf, n_rope = make_c2_step(torch, coda, T, dims, p["eps"])
+    flops = c2_flops(*dims)
+    total_flops = sum(flops.values())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    tm = OpTimer(torch)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step(tm)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    op_ms = tm.mean_ms()
+
+    value = total_flops / (ms_step * 1e-3) / 1e12
+    dom = "rope"
+    dom_ms = op_ms[dom]
+    achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
+    ops = {}
+    for k, v in op_ms.items():
+        ent = {"us": round(v * 1e3, 2)}
+        if k in flops:
+            tf = flops[k] / (v * 1e-3) / 1e12
+            ent.update(tflops=round(tf, 1), pct_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2))
+        ops[k] = ent
+    log("per-op (HIP events on the launch stream):")
+    for k, v in ops.items():
+        log(f"  {k:10s} {v}")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(p, dims, n_rope)
+        log(f"cpu oracle: {cpu}")
+
+    if args.all:
+        rows = bench_all(torch, coda, synth)
+        if args.out:
+            with open(args.out, "w") as f:
+                for r_ in rows:
+                    f.write(json.dumps(r_) + "\n")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {
+            "workload": "GEMM->residual->RMSNorm->GEMM forward, Llama-3-1B-like: M=8192 tokens (4x2048), d=2048, "
+                        "W1 2048x2048 (rowscale) and QKV W1 2048x3072 with RoPE (theta=5e5, hd=64)",
+            "M": M, "d": d, "K": K, "N": N, "N_qkv": NR, "n_rope": n_rope,
+            "calls": ["coda_gemm_res_sumsq", "coda_row_rms", "coda_gemm_rowscale", "coda_gemm_rope"],
+        },
+        "ops": ops,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "coda_gemm_rope (8192x3072x2048)",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": load_traffic("rope_c2"),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
