@@ -27,13 +27,17 @@
 // MFMA fragment read is always one ds_read_b128 per lane.
 //
 // Pipeline.  256 threads = 4 waves in a 2x2 grid over a BF x BT output tile
-// (BF = 256 features, BT = 256 tokens), BK = 64, two LDS stages (128 KiB):
-// the global loads of k-tile kt+1 are issued before the MFMAs of k-tile kt
-// and written to the other LDS stage after them; one barrier per k-tile.
+// (BF = 256 features, BT = 256 tokens), BK = 64, two LDS stages (128 KiB).
+// MFMA fragments are double-buffered in registers (the reads of k-step s+1
+// overlap the MFMAs of k-step s); global loads run two k-tiles ahead through
+// one register staging set; one barrier per k-tile, placed inside its last
+// k-step so that MFMAs are queued on both sides of it.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace coda {
 
@@ -107,60 +111,71 @@ struct TileCopy {
   static constexpr int NCH = KMAJ ? (ROWS * KCH) / NT : 8;
   static constexpr int NBLK = ROWS;                     // 8x8 blocks (MN-major)
   u32x4 v[NCH];
+  uint32_t ok = 0;  // bit i: chunk i is inside the matrix (else it is stored as zeros)
 
-  // K-major: element (row, k) at g[row * ld + k].  MN-major: at g[k * ld + row].
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int ld, int row0, int nrows,
-                                       int k0, int K, int tid) {
+  // Load chunk i of the k-tile starting at k0.  K-major: element (row, k) at
+  // g[row * ld + k]; MN-major: at g[k * ld + row], chunk i = the 16 bytes of
+  // k-row kb*8 + i of this thread's 8x8 block.  Raw buffer loads through a
+  // scalar descriptor based at the tile origin (range 4 GiB, so no hardware
+  // range check is relied on); a masked chunk loads offset 0 (a valid
+  // element) and is zeroed when written to LDS: branch-free and wait-free.
+  __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ g, int ld, int row0, int nrows,
+                                             int k0, int K, int tid, int i) {
+    bool in;
+    uint32_t off;
+    __amdgpu_buffer_rsrc_t rs;
     if constexpr (KMAJ) {
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int idx = i * NT + tid;
-        const int row = idx / KCH, ck = idx % KCH;
-        const int gr = row0 + row, gk = k0 + ck * 8;
-        if (gr < nrows && gk < K)
-          v[i] = ld16(g + (size_t)gr * ld + gk);
-        else
-          v[i] = (u32x4){0u, 0u, 0u, 0u};
-      }
+      rs = __builtin_amdgcn_make_buffer_rsrc((void*)(g + (size_t)row0 * ld + k0), (short)0, -1, 0x00020000);
+      const int idx = i * NT + tid;
+      const int row = idx / KCH, ck = idx % KCH;
+      in = row0 + row < nrows && k0 + ck * 8 < K;
+      off = (uint32_t)(row * ld + ck * 8) * 2u;
     } else {
+      rs = __builtin_amdgcn_make_buffer_rsrc((void*)(g + (size_t)k0 * ld + row0), (short)0, -1, 0x00020000);
       const int rb = tid % (ROWS / 8), kb = tid / (ROWS / 8);
-      const int gr = row0 + rb * 8;
-      const bool act = tid < NBLK && gr < nrows;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int gk = k0 + kb * 8 + j;
-        if (act && gk < K)
-          v[j] = ld16(g + (size_t)gk * ld + gr);
-        else
-          v[j] = (u32x4){0u, 0u, 0u, 0u};
+      in = tid < NBLK && row0 + rb * 8 < nrows && k0 + kb * 8 + i < K;
+      off = (uint32_t)((kb * 8 + i) * ld + rb * 8) * 2u;
+    }
+    ok = (ok & ~(1u << i)) | ((uint32_t)in << i);
+    v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, in ? off : 0u, 0, 0));
+  }
+
+  __device__ __forceinline__ u32x4 masked(int i) const {
+    return ((ok >> i) & 1u) ? v[i] : (u32x4){0u, 0u, 0u, 0u};
+  }
+
+  // Write chunk i to the K-major LDS tile.  MN-major: row i of the transposed
+  // 8x8 block (needs all eight loaded chunks).
+  __device__ __forceinline__ void store_chunk(char* s, int tid, int i) const {
+    if constexpr (KMAJ) {
+      const int idx = i * NT + tid;
+      const int row = idx / KCH, ck = idx % KCH;
+      st16(s + lds_off(row, ck), masked(i));
+    } else {
+      if constexpr (NBLK < NT) {
+        if (tid >= NBLK) return;
       }
+      const int rb = tid % (ROWS / 8), kb = tid / (ROWS / 8);
+      // chunk j holds k = kb*8 + j for rows rb*8 .. rb*8+7 (row 2d in the low
+      // half of dword d); transposed row i packs k pairs (2q, 2q+1).
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t a = masked(2 * q)[i >> 1], b = masked(2 * q + 1)[i >> 1];
+        o[q] = (i & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      }
+      st16(s + lds_off(rb * 8 + i, kb), o);
     }
   }
 
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ g, int ld, int row0, int nrows, int k0,
+                                       int K, int tid) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) load_chunk(g, ld, row0, nrows, k0, K, tid, i);
+  }
   __device__ __forceinline__ void store(char* s, int tid) const {
-    if constexpr (KMAJ) {
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int idx = i * NT + tid;
-        const int row = idx / KCH, ck = idx % KCH;
-        st16(s + lds_off(row, ck), v[i]);
-      }
-    } else {
-      if (tid >= NBLK) return;
-      const int rb = tid % (ROWS / 8), kb = tid / (ROWS / 8);
-      // v[j] holds k = kb*8 + j for rows rb*8 .. rb*8+7 (row 2d in the low half
-      // of dword d).  Row r of the transposed block packs k pairs (2i, 2i+1).
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        u32x4 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t a = v[2 * i][r >> 1], b = v[2 * i + 1][r >> 1];
-          o[i] = (r & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-        }
-        st16(s + lds_off(rb * 8 + r, kb), o);
-      }
-    }
+    for (int i = 0; i < NCH; ++i) store_chunk(s, tid, i);
   }
 };
 
@@ -250,42 +265,139 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
   for (int j = 0; j < CI; ++j) b_row[j] = wt * WT + j * 32 + lt;
 
   const int nk = (p.K + BK - 1) / BK;
-  ca.load(p.W, p.ldw, f0, p.F, 0, p.K, tid);
-  cb.load(p.X, p.ldx, t0, p.T, 0, p.K, tid);
-  ca.store(smem, tid);
-  cb.store(smem + A_BYTES, tid);
-  __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * STAGE;
-    char* nxt = smem + ((kt + 1) & 1) * STAGE;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      ca.load(p.W, p.ldw, f0, p.F, (kt + 1) * BK, p.K, tid);
-      cb.load(p.X, p.ldx, t0, p.T, (kt + 1) * BK, p.K, tid);
-    }
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int ck = 2 * s + hh;
-      bf16x8 a[RI], b[CI];
-#pragma unroll
-      for (int i = 0; i < RI; ++i)
-        a[i] = __builtin_bit_cast(bf16x8, ld16(cur + lds_off(a_row[i], ck)));
-#pragma unroll
-      for (int j = 0; j < CI; ++j)
-        b[j] = __builtin_bit_cast(bf16x8, ld16(cur + A_BYTES + lds_off(b_row[j], ck)));
-#pragma unroll
-      for (int i = 0; i < RI; ++i)
-#pragma unroll
-        for (int j = 0; j < CI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      ca.store(nxt, tid);
-      cb.store(nxt + A_BYTES, tid);
+  // ---- building blocks of the explicitly scheduled k-loop -------------------
+  constexpr int NP = RI * CI / 2;     // MFMA pairs per k-step
+  constexpr int NRD = RI + CI;        // fragment reads per k-step
+  constexpr int RPP = (NRD + NP - 1) / NP;
+  constexpr int NCA = TileCopy<BF, WK>::NCH, NCB = TileCopy<BT, XK>::NCH;
+  constexpr int APP = (NCA + NP - 1) / NP, BPP = (NCB + NP - 1) / NP;
+  constexpr int HP = NP / 2;          // pairs before the barrier in step 3
+
+  auto read_one = [&](const char* st, int s, int q, bf16x8 (&a)[RI], bf16x8 (&b)[CI]) {
+    const int ck = 2 * s + hh;
+    if (q < RI)
+      a[q] = __builtin_bit_cast(bf16x8, ld16(st + lds_off(a_row[q], ck)));
+    else if (q < NRD)
+      b[q - RI] = __builtin_bit_cast(bf16x8, ld16(st + A_BYTES + lds_off(b_row[q - RI], ck)));
+  };
+  auto mfma_pair = [&](const bf16x8 (&a)[RI], const bf16x8 (&b)[CI], int pr) {
+    constexpr int JP = CI / 2;
+    const int i = pr / JP, j = 2 * (pr % JP);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    acc[i][j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j + 1], acc[i][j + 1], 0, 0, 0);
+  };
+  auto load_a = [&](int k0, int i) { ca.load_chunk(p.W, p.ldw, f0, p.F, k0, p.K, tid, i); };
+  auto load_b = [&](int k0, int i) { cb.load_chunk(p.X, p.ldx, t0, p.T, k0, p.K, tid, i); };
+
+  // Prologue: k-tile 0 to LDS stage 0, k-tile 1 to the staging registers.
+  // With no k-tile (K == 0) nothing is loaded: an empty operand may have no
+  // storage at all, and masked chunks read the tile origin, which then does
+  // not exist.  Every load below has k0 < K and a tile origin inside the
+  // matrix, so its offset-0 fallback is a real element.
+  bf16x8 fa0[RI], fb0[CI], fa1[RI], fb1[CI];
+  if (nk > 0) {
+    ca.load(p.W, p.ldw, f0, p.F, 0, p.K, tid);
+    cb.load(p.X, p.ldx, t0, p.T, 0, p.K, tid);
+    ca.store(smem, tid);
+    cb.store(smem + A_BYTES, tid);
+    if (nk > 1) {
+      ca.load(p.W, p.ldw, f0, p.F, BK, p.K, tid);
+      cb.load(p.X, p.ldx, t0, p.T, BK, p.K, tid);
     }
     __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NRD; ++q) read_one(smem, 0, q, fa0, fb0);
   }
+
+  // One k-tile: four k-steps of NP MFMA pairs.  Each pair carries side work:
+  // the fragment reads of the next k-step (into the other register set); in
+  // step 2 the write of k-tile kt+1 from the staging registers to the other
+  // LDS stage and, for K-major operands, the refill of each chunk with
+  // k-tile kt+2; in step 3 the refill of MN-major operands, then the single
+  // barrier, then the first fragment reads of k-tile kt+1.  sched_barrier
+  // fences keep every piece in this order.
+  auto ktile = [&](int kt, auto has1_c, auto has2_c) {
+    constexpr bool HAS1 = decltype(has1_c)::value, HAS2 = decltype(has2_c)::value;
+    const char* cur = smem + (kt & 1) * STAGE;
+    char* nxt = smem + ((kt + 1) & 1) * STAGE;
+    const int k2 = (kt + 2) * BK;
+    // steps 0 and 1
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+      mfma_pair(fa0, fb0, pr);
+#pragma unroll
+      for (int r = 0; r < RPP; ++r) read_one(cur, 1, pr * RPP + r, fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+      mfma_pair(fa1, fb1, pr);
+#pragma unroll
+      for (int r = 0; r < RPP; ++r) read_one(cur, 2, pr * RPP + r, fa0, fb0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // step 2
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+      mfma_pair(fa0, fb0, pr);
+#pragma unroll
+      for (int r = 0; r < RPP; ++r) read_one(cur, 3, pr * RPP + r, fa1, fb1);
+      if constexpr (HAS1) {
+#pragma unroll
+        for (int c = 0; c < APP; ++c) {
+          const int i = pr * APP + c;
+          if (i < NCA) {
+            ca.store_chunk(nxt, tid, i);
+            if constexpr (HAS2 && WK) load_a(k2, i);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < BPP; ++c) {
+          const int i = pr * BPP + c;
+          if (i < NCB) {
+            cb.store_chunk(nxt + A_BYTES, tid, i);
+            if constexpr (HAS2 && XK) load_b(k2, i);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // step 3, first half: MN-major refills
+#pragma unroll
+    for (int pr = 0; pr < HP; ++pr) {
+      mfma_pair(fa1, fb1, pr);
+      if constexpr (HAS2 && !WK) {
+#pragma unroll
+        for (int c = 0; c < (NCA + HP - 1) / HP; ++c)
+          if (pr * ((NCA + HP - 1) / HP) + c < NCA) load_a(k2, pr * ((NCA + HP - 1) / HP) + c);
+      }
+      if constexpr (HAS2 && !XK) {
+#pragma unroll
+        for (int c = 0; c < (NCB + HP - 1) / HP; ++c)
+          if (pr * ((NCB + HP - 1) / HP) + c < NCB) load_b(k2, pr * ((NCB + HP - 1) / HP) + c);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    // step 3, second half: first fragments of k-tile kt+1
+    constexpr int RPH = (NRD + (NP - HP) - 1) / (NP - HP);
+#pragma unroll
+    for (int pr = HP; pr < NP; ++pr) {
+      mfma_pair(fa1, fb1, pr);
+      if constexpr (HAS1) {
+#pragma unroll
+        for (int r = 0; r < RPH; ++r) read_one(nxt, 0, (pr - HP) * RPH + r, fa0, fb0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) ktile(kt, T_{}, T_{});
+  if (kt + 1 < nk) ktile(kt++, T_{}, F_{});
+  if (kt < nk) ktile(kt, F_{}, F_{});
 
   Geom g;
   g.fw0 = f0 + wf * WF;
