@@ -19,20 +19,20 @@
 // reductions are in-lane adds plus one exchange between lanes l and l^32, and
 // every store is a 16-byte vector store.
 //
-// Operand layouts.  Each operand is either K-contiguous ("K-major") or
-// contiguous along its feature/token index ("MN-major").  Both are staged to
-// the same K-major, XOR-swizzled LDS tile: K-major tiles are copied with
-// 16-byte loads; MN-major tiles are read as 8x8 bf16 blocks (eight coalesced
-// 16-byte loads) and transposed in registers before the LDS write, so the
-// MFMA fragment read is always one ds_read_b128 per lane.
+// Operand staging.  Both operand tiles go from global memory straight to LDS
+// with the gfx950 LDS-DMA buffer load (16 bytes per lane; lane L of one
+// instruction lands at LDS base + 16 L), so no VGPR staging or ds_write is
+// spent on them.  A K-contiguous ("K-major") tile is stored row-contiguous
+// (128 bytes per row, 16-byte chunks XOR-swizzled by (row >> 1) & 7) and each
+// MFMA fragment is one ds_read_b128.  A tile contiguous along its
+// feature/token index ("MN-major") is stored as 64 k-rows (32-byte blocks
+// XOR-swizzled by (k & 3) << 1) and its fragments come from two transposing
+// reads (ds_read_b64_tr_b16): within a group of 16 lanes, lane j receives
+// element j % 4 of the 8 bytes addressed by lane j / 4 + 4 m (m = 0..3).  All
+// DMA writes cover whole 128/512-byte global rows per instruction, and every
+// fragment read phase touches each LDS bank once.  Out-of-matrix chunks use an
+// offset beyond the descriptor's range, for which the hardware writes zeros.
 //
-// Pipeline.  256 threads = 4 waves in a 2x2 grid over a BF x BT output tile
-// (BF = 256 features, BT = 256 tokens), BK = 64, two LDS stages (128 KiB).
-// MFMA fragments are double-buffered in registers (the reads of k-step s+1
-// overlap the MFMAs of k-step s); global loads run two k-tiles ahead through
-// one register staging set; one barrier per k-tile, placed inside its last
-// k-step so that MFMAs are queued on both sides of it.  Interior tiles with
-// K % 64 == 0 take an unmasked copy path; edge tiles a masked one.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -85,135 +85,128 @@ __device__ __forceinline__ u32x4 pack8(const float (&v)[8]) {
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// ---------------------------------------------------------------------------
-// LDS tile layout ("k-step major").  One operand tile of ROWS rows x BK = 64
-// k is stored as four slabs, one per 16-wide MFMA k-step; a slab holds, for
-// each row, 32 bytes (two 16-byte halves: k 0-7 and k 8-15 of the step).
-// Rows are grouped by 8 (256 bytes per group); inside a group the row's
-// 32-byte slot is (row & 7) ^ ((row >> 4) & 7) and its halves are swapped
-// when (row >> 3) is odd.  With this swizzle every 16-lane phase of
-//   - an MFMA fragment read (16 consecutive rows, one half),
-//   - a K-major tile write (8 rows x both halves),
-//   - a transposed MN-major tile write (16 row groups, one row each)
-// touches 16 distinct 16-byte slots of a 256-byte window, i.e. all 64 banks
-// once; and the fragment address of a lane depends only on its row, so the
-// k-step and the LDS stage become immediate offsets of ds_read_b128.
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ int slab_off(int row, int half) {
-  return ((row >> 3) << 8) + ((((row & 7) ^ ((row >> 4) & 7))) << 5) + ((half ^ ((row >> 3) & 1)) << 4);
-}
-
 // Feature permutation of one 32-row MFMA block (see file header).
 __device__ __forceinline__ int phi32(int i) {
   const int g = i >> 3, h = (i >> 2) & 1, v = i & 3;
   return ((g >> 1) << 4) + (h << 3) + ((g & 1) << 2) + v;
 }
 
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One LDS-DMA instruction: 16 bytes per lane from buffer(base, range) at
+// byte offset voff to LDS dst + 16 * lane (dst wave-uniform).  Issued as
+// inline assembly so that the compiler's wait insertion does not make every
+// later LDS read wait for all DMA in flight; completion is awaited explicitly
+// (wait_vmcnt) before the barrier that publishes the stage.  vmcnt counts in
+// issue order, so waits the compiler inserts for its own later loads stay
+// correct (they may only wait longer).
+__device__ __forceinline__ void dma16(const void* base, uint32_t range, uint32_t voff, char* dst) {
+  typedef __attribute__((ext_vector_type(4))) int i32x4;
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  i32x4 rs;
+  rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));  // stride 0
+  rs[2] = __builtin_amdgcn_readfirstlane((int)range);
+  rs[3] = 0x00020000;
+  const int m0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_ptr_t)dst);
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 4\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rs), "s"(m0)
+      : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N), other counters unconstrained (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // ---------------------------------------------------------------------------
-// Global -> register -> LDS copy of one operand tile (ROWS x BK).
+// One operand tile: ROWS rows (features or tokens) x BK = 64 k, in one LDS
+// stage of REGION bytes.  Thread (wave w, lane l) issues NCH DMA instructions
+// per k-tile; instruction i of wave w fills the 1 KiB LDS block 4 i + w.
 //
-// K-major (element (row, k) at g[row * ld + k]): chunk i of thread
-// (wave w, lane l) is row i*32 + w*8 + ((l>>1)&7), k-chunk 2*(l>>4) + (l&1);
-// a wave instruction reads 8 whole 128-byte rows.  MN-major (element at
-// g[k * ld + row], ROWS == 256): thread t owns the 8x8 block of rows
-// (t%32)*8.. and k (t/32)*8..; chunk j is k-row j of the block (a wave
-// instruction reads two 512-byte row segments) and is transposed in
-// registers before the LDS write.
-//
-// Loads are raw buffer loads through a scalar descriptor based at the tile
-// origin of the k-tile (range 4 GiB; no hardware range check is relied on).
-// The per-chunk stride goes in the scalar soffset.  MASKED variants (edge
-// tiles, ragged K) replace an out-of-matrix chunk's offset by 0 (the tile
-// origin, a real element) and zero the chunk when it is written to LDS.
+// K-major (element (row, k) at g[row * ld + k]): block 4i+w holds rows
+//   (4i+w)*8 .. +7; lane l loads row (4i+w)*8 + l/8, logical chunk
+//   (l%8) ^ sw(row), sw(row) = (row >> 1) & 7 = (4w + l/16) & 7.
+// MN-major (element (row, k) at g[k * ld + row], ROWS = 256): block 4i+w holds
+//   k-rows (4i+w)*2 .. +1 (512 bytes each); lane l loads k-row (4i+w)*2 + l/32,
+//   logical chunk c with 32-byte block (p/2) ^ ((k & 3) << 1), p = l % 32.
 // ---------------------------------------------------------------------------
 
 template <int ROWS, bool KMAJ>
-struct TileCopy {
+struct Operand {
   static_assert(ROWS == 128 || ROWS == 256, "tile rows");
   static_assert(KMAJ || ROWS == 256, "MN-major operands use 256-row tiles");
-  static constexpr int NCH = KMAJ ? ROWS / 32 : 8;   // 16-byte chunks per thread
-  static constexpr int SLAB = ROWS * 32;               // bytes per k-step slab
-  static constexpr int REGION = ROWS * BK * 2;         // bytes per LDS stage
-  u32x4 v[NCH];
-  uint32_t ok = 0;      // MASKED only: bit i set = chunk i is inside the matrix
-  uint32_t voff = 0;    // per-thread byte offset of chunk 0 from the tile origin
-  int wbase[4];         // LDS write offsets (K-major: chunks i and i+4; MN-major: wbase[0])
-  int sld2 = 0;         // 2 * ld (bytes per k-row or per row)
-  int lrow = 0, lk = 0; // (MASKED) row and k of chunk 0 relative to the tile origin
+  static constexpr int REGION = ROWS * BK * 2;           // bytes per stage
+  static constexpr int NCH = REGION / (NT * 16);          // DMA instructions per thread
+  uint32_t voff = 0;  // byte offset of chunk 0 from the k-tile origin
+  uint32_t vstep = 0; // byte offset between chunks i and i+1
+  int lrow = 0;       // (masking) row or k-row of chunk 0 relative to the tile origin
+  int lcol = 0;       // (masking) k (K-major) or row (MN-major) of chunk 0
 
-  __device__ __forceinline__ void init(int ld, int tid) {
-    const int w = tid >> 6, l = tid & 63;
-    sld2 = 2 * ld;
+  __device__ __forceinline__ void init(int ld, int w, int l) {
     if constexpr (KMAJ) {
-      const int q = (l >> 1) & 7, ck = 2 * (l >> 4) + (l & 1);
-      lrow = w * 8 + q;
-      lk = ck * 8;
-      voff = (uint32_t)(lrow * ld + lk) * 2u;
-      const int s = l >> 4, h = l & 1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wbase[i] = s * SLAB + slab_off(i * 32 + lrow, h);
+      const int row = w * 8 + (l >> 3);
+      const int c = (l & 7) ^ ((w * 4 + (l >> 4)) & 7);
+      lrow = row;
+      lcol = c * 8;
+      voff = (uint32_t)(row * ld + c * 8) * 2u;
+      vstep = (uint32_t)(32 * ld) * 2u;
     } else {
-      const int rb = tid & 31, kb = tid >> 5;
-      lrow = rb * 8;
-      lk = kb * 8;
-      voff = (uint32_t)(lk * ld + lrow) * 2u;
-      wbase[0] = (kb >> 1) * SLAB + slab_off(rb * 8, kb & 1);  // row 0 of the block
+      const int kr = w * 2 + (l >> 5), pp = l & 31;
+      const int c = (((pp >> 1) ^ ((kr & 3) << 1)) << 1) | (pp & 1);
+      lrow = kr;
+      lcol = c * 8;
+      voff = (uint32_t)(kr * ld + c * 8) * 2u;
+      vstep = (uint32_t)(8 * ld) * 2u;
     }
   }
 
-  // Stride of chunk i from chunk 0, in bytes (uniform).
-  __device__ __forceinline__ int soff(int i) const { return KMAJ ? i * 32 * sld2 : i * sld2; }
-
+  // DMA chunk i of the k-tile at k0 into the stage at LDS byte offset `stage`
+  // (wave-uniform: instruction i of wave w writes block 4 i + w).
   template <bool MASKED>
-  __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ g, int ld, int row0, int nrows,
-                                             int k0, int K, int i) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(g + (KMAJ ? (size_t)row0 * ld + k0 : (size_t)k0 * ld + row0)), (short)0, -1, 0x00020000);
-    if constexpr (!MASKED) {
-      v[i] = buf_load16(rs, voff, soff(i));
-    } else {
-      const bool in = KMAJ ? (row0 + lrow + 32 * i < nrows && k0 + lk < K)
-                           : (row0 + lrow < nrows && k0 + lk + i < K);
-      ok = (ok & ~(1u << i)) | ((uint32_t)in << i);
-      v[i] = buf_load16(rs, in ? voff + (uint32_t)soff(i) : 0u, 0);
+  __device__ __forceinline__ void dma(const uint16_t* __restrict__ g, int ld, int row0, int nrows, int k0,
+                                      int K, char* smem_base, int stage, int w, int i) const {
+    const uint16_t* base = KMAJ ? g + (size_t)row0 * ld + k0 : g + (size_t)k0 * ld + row0;
+    uint32_t off = voff + (uint32_t)i * vstep;
+    int range = 0x7fffffff;
+    if constexpr (MASKED) {
+      // Bytes from the tile origin to the end of the last valid row (K-major)
+      // or k-row (MN-major); chunks beyond it, or past K / nrows inside a
+      // row, get an offset beyond the range and are written as zeros.
+      const long long span = KMAJ ? (long long)(nrows - row0 - 1) * ld + (K - k0)
+                                  : (long long)(K - k0 - 1) * ld + (nrows - row0);
+      range = (int)(span * 2 < 0x7fffffffLL ? span * 2 : 0x7fffffffLL);
+      const bool in = KMAJ ? (k0 + lcol < K) : (row0 + lcol < nrows);
+      off = in ? off : 0x80000000u;
     }
-  }
-
-  template <bool MASKED>
-  __device__ __forceinline__ u32x4 chunk(int i) const {
-    if constexpr (!MASKED) return v[i];
-    return ((ok >> i) & 1u) ? v[i] : (u32x4){0u, 0u, 0u, 0u};
-  }
-
-  // Write chunk i (MN-major: transposed row i of the thread's block).
-  template <bool MASKED>
-  __device__ __forceinline__ void store_chunk(char* s, int i) const {
-    if constexpr (KMAJ) {
-      st16(s + wbase[i & 3] + (i >> 2) * 4096, chunk<MASKED>(i));
-    } else {
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t a = chunk<MASKED>(2 * q)[i >> 1], b = chunk<MASKED>(2 * q + 1)[i >> 1];
-        o[q] = (i & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-      }
-      st16(s + (wbase[0] ^ (i << 5)), o);
-    }
+    char* dst = smem_base + stage + (4 * i + w) * 1024;
+    dma16(base, (uint32_t)range, off, dst);
   }
 };
 
-// First-use order of the RI + CI fragments of one k-step for the MFMA pair
-// sequence pr -> (i = pr / (CI/2), j = 2*(pr % (CI/2)), j+1): a0, b0..b(CI-1),
-// a1..a(RI-1).  Returns the fragment index (< RI: operand A row block i,
-// else RI + column block j).
-template <int RI, int CI>
-__device__ __forceinline__ constexpr int frag_order(int n) {
-  return n == 0 ? 0 : (n <= CI ? RI + n - 1 : n - CI);
+// Per-lane LDS byte offset (within an operand's stage region) of an MFMA
+// fragment: K-major row `row`, k half `hh` of k-step 0 (other k-steps: XOR
+// (s << 5)); MN-major: the transposing-read address for feature/token block
+// starting at `row0` (32 rows), k half hh, k-step 0, sub-read 0 (other
+// k-steps / sub-reads: + (16 s + 4 u) * 512).
+__device__ __forceinline__ int kmaj_frag_off(int row, int hh) {
+  return row * 128 + ((hh ^ ((row >> 1) & 7)) << 4);
+}
+template <bool PHI>
+__device__ __forceinline__ int mnmaj_frag_off(int row0, int lane) {
+  const int G = lane >> 4, q = lane & 15;
+  const int kr = 8 * (G >> 1) + (q >> 2);
+  const int r = 16 * (G & 1) + 4 * (q & 3);
+  const int f = row0 + (PHI ? phi32(r) : r);
+  const int blk = f >> 4;
+  return kr * 512 + ((blk ^ ((kr & 3) << 1)) << 5) + ((f & 15) << 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -275,14 +268,15 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
   constexpr int WF = BF / WGF, WT = BT / WGT;
   static_assert(WF == WAVE_F, "row partials assume 128-feature wave tiles");
   constexpr int RI = WF / 32, CI = WT / 32;
-  using CA = TileCopy<BF, WK>;
-  using CB = TileCopy<BT, XK>;
-  // LDS: A stage 0 | A stage 1 | B stage 0 | B stage 1
-  constexpr int A_REG = CA::REGION, B_REG = CB::REGION, B_OFF = 2 * A_REG;
+  using OA = Operand<BF, WK>;
+  using OB = Operand<BT, XK>;
+  // LDS: A stage 0 | A stage 1 | B stage 0 | B stage 1 (stage bit = bit 15 or 14)
+  constexpr int A_REG = OA::REGION, B_REG = OB::REGION, B_OFF = 2 * A_REG;
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * (A_REG + B_REG)];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * (A_REG + B_REG)];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf = wave % WGF, wt = wave / WGF;
   const int lt = lane & 31, hh = lane >> 5;
   int tf, tt;
@@ -295,38 +289,78 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
 #pragma unroll
     for (int j = 0; j < CI; ++j) acc[i][j] = (f32x16){};
 
-  // Per-lane LDS fragment offsets (k-step and stage are immediates).
+  // Per-lane fragment offsets (stage and k-step are added per read).
   int a_off[RI], b_off[CI];
 #pragma unroll
-  for (int i = 0; i < RI; ++i) a_off[i] = slab_off(wf * WF + i * 32 + phi32(lt), hh);
+  for (int i = 0; i < RI; ++i)
+    a_off[i] = WK ? kmaj_frag_off(wf * WF + i * 32 + phi32(lt), hh) : mnmaj_frag_off<true>(wf * WF + i * 32, lane);
 #pragma unroll
-  for (int j = 0; j < CI; ++j) b_off[j] = B_OFF + slab_off(wt * WT + j * 32 + lt, hh);
+  for (int j = 0; j < CI; ++j)
+    b_off[j] = B_OFF + (XK ? kmaj_frag_off(wt * WT + j * 32 + lt, hh) : mnmaj_frag_off<false>(wt * WT + j * 32, lane));
 
-  CA ca;
-  CB cb;
-  ca.init(p.ldw, tid);
-  cb.init(p.ldx, tid);
+  OA oa;
+  OB ob;
+  oa.init(p.ldw, wave, lane);
+  ob.init(p.ldx, wave, lane);
 
   const int nk = (p.K + BK - 1) / BK;
   const bool interior = f0 + BF <= p.F && t0 + BT <= p.T && p.K % BK == 0;
 
-  constexpr int NP = RI * CI / 2;     // MFMA pairs per k-step
-  constexpr int NRD = RI + CI;        // fragment reads per k-step
+  constexpr int NP = RI * CI / 2;           // MFMA pairs per k-step
+  constexpr int NRA = WK ? RI : 2 * RI;     // LDS reads for operand A per k-step
+  constexpr int NRB = XK ? CI : 2 * CI;
+  constexpr int NRD = NRA + NRB;
   constexpr int RPP = (NRD + NP - 1) / NP;
-  constexpr int HP = NP / 2;          // pairs before the barrier in step 3
+  constexpr int HP = NP / 2;                // pairs before the barrier in step 3
   constexpr int RPH = (NRD + (NP - HP) - 1) / (NP - HP);
+  constexpr int NDMA = OA::NCH + OB::NCH;
+  constexpr int DPP = (NDMA + (NP - HP) - 1) / (NP - HP);
 
   bf16x8 fa0[RI], fb0[CI], fa1[RI], fb1[CI];
 
-  // stage = 0 or 1 (runtime): byte offsets stage*A_REG / stage*B_REG are one
-  // VALU add per fragment per k-tile; the k-step is an immediate offset.
+  // Read n (first-use order: a0, b0.., a1..) of k-step s from `stage` (0/1).
+  // MN-major fragments take two transposing reads (n and n+1 of the same
+  // fragment fill its low and high halves).
   auto read_one = [&](int stage, int s, int n, bf16x8 (&a)[RI], bf16x8 (&b)[CI]) {
     if (n >= NRD) return;
-    const int q = frag_order<RI, CI>(n);
-    if (q < RI)
-      a[q] = __builtin_bit_cast(bf16x8, ld16(smem + (a_off[q] + stage * A_REG) + s * CA::SLAB));
-    else
-      b[q - RI] = __builtin_bit_cast(bf16x8, ld16(smem + (b_off[q - RI] + stage * B_REG) + s * CB::SLAB));
+    // order: fragment index q and (for MN-major) sub-read u
+    int q, u = 0;
+    {
+      const int na = WK ? 1 : 2;  // reads per A fragment
+      const int nb = XK ? 1 : 2;
+      if (n < na) {
+        q = 0;
+        u = n;
+      } else if (n < na + CI * nb) {
+        q = RI + (n - na) / nb;
+        u = (n - na) % nb;
+      } else {
+        q = 1 + (n - na - CI * nb) / na;
+        u = (n - na - CI * nb) % na;
+      }
+    }
+    if (q < RI) {
+      if constexpr (WK) {
+        a[q] = __builtin_bit_cast(bf16x8, ld16(smem + ((a_off[q] ^ (s << 5)) + stage * A_REG)));
+      } else {
+        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+        const bf16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(lds_ptr_t)(smem + a_off[q] + stage * A_REG + (16 * s + 4 * u) * 512));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[q][4 * u + e] = h[e];
+      }
+    } else {
+      const int j = q - RI;
+      if constexpr (XK) {
+        b[j] = __builtin_bit_cast(bf16x8, ld16(smem + ((b_off[j] ^ (s << 5)) + stage * B_REG)));
+      } else {
+        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+        const bf16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(lds_ptr_t)(smem + b_off[j] + stage * B_REG + (16 * s + 4 * u) * 512));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[j][4 * u + e] = h[e];
+      }
+    }
   };
   auto mfma_pair = [&](const bf16x8 (&a)[RI], const bf16x8 (&b)[CI], int pr) {
     constexpr int JP = CI / 2;
@@ -338,45 +372,40 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
   // The whole k-loop for one masking mode (uniform per workgroup).
   auto mainloop = [&](auto masked_c) {
     constexpr bool MASKED = decltype(masked_c)::value;
-    auto load_a = [&](int k0, int i) { ca.template load_chunk<MASKED>(p.W, p.ldw, f0, p.F, k0, p.K, i); };
-    auto load_b = [&](int k0, int i) { cb.template load_chunk<MASKED>(p.X, p.ldx, t0, p.T, k0, p.K, i); };
+    // DMA instruction d (0..NDMA-1) of the k-tile at k0 into stage `st`.
+    auto dma = [&](int k0, int st, int d) {
+      if (d < OA::NCH)
+        oa.template dma<MASKED>(p.W, p.ldw, f0, p.F, k0, p.K, smem, st * A_REG, wave, d);
+      else if (d < NDMA)
+        ob.template dma<MASKED>(p.X, p.ldx, t0, p.T, k0, p.K, smem + B_OFF, st * B_REG, wave, d - OA::NCH);
+    };
 
-    // Prologue: k-tile 0 to LDS stage 0, k-tile 1 to the staging registers.
-    // Every load has k0 < K and a tile origin inside its matrix, so the
-    // offset-0 fallback of a masked chunk is a real element; with no k-tile
-    // nothing is loaded (an empty operand may have no storage at all).
+    // Prologue: k-tiles 0 and 1 into stages 0 and 1.  With no k-tile nothing
+    // is loaded (an empty operand may have no storage at all).  Every DMA has
+    // k0 < K and a tile origin inside its matrix.
     if (nk > 0) {
 #pragma unroll
-      for (int i = 0; i < CA::NCH; ++i) load_a(0, i);
-#pragma unroll
-      for (int i = 0; i < CB::NCH; ++i) load_b(0, i);
-#pragma unroll
-      for (int i = 0; i < CA::NCH; ++i) ca.template store_chunk<MASKED>(smem, i);
-#pragma unroll
-      for (int i = 0; i < CB::NCH; ++i) cb.template store_chunk<MASKED>(smem + B_OFF, i);
+      for (int d = 0; d < NDMA; ++d) dma(0, 0, d);
       if (nk > 1) {
 #pragma unroll
-        for (int i = 0; i < CA::NCH; ++i) load_a(BK, i);
-#pragma unroll
-        for (int i = 0; i < CB::NCH; ++i) load_b(BK, i);
+        for (int d = 0; d < NDMA; ++d) dma(BK, 1, d);
+        wait_vmcnt<NDMA>();
+      } else {
+        wait_vmcnt<0>();
       }
       __syncthreads();
 #pragma unroll
       for (int n = 0; n < NRD; ++n) read_one(0, 0, n, fa0, fb0);
     }
 
-    // One k-tile: four k-steps of NP MFMA pairs.  Each pair carries side
-    // work: a fragment read of the next k-step (other register set, in
-    // first-use order); in step 2 the write of k-tile kt+1 from the staging
-    // registers to the other LDS stage and, for K-major operands, the refill
-    // of each chunk with k-tile kt+2; in step 3 the refill of MN-major
-    // operands, then the single barrier, then the first fragment reads of
-    // k-tile kt+1.  sched_barrier fences keep every piece in this order.
+    // One k-tile: four k-steps of NP MFMA pairs, each pair carrying the
+    // fragment reads of the next k-step (other register set).  In step 3,
+    // after half the MFMAs: wait for k-tile kt+1's DMA, barrier, then the
+    // first fragment reads of k-tile kt+1 and the DMA of k-tile kt+2 into
+    // the stage k-tile kt has released.  sched_barrier fences keep the order.
     auto ktile = [&](int kt, auto has1_c, auto has2_c) {
-      const int ST = kt & 1, NS = ST ^ 1;
       constexpr bool HAS1 = decltype(has1_c)::value, HAS2 = decltype(has2_c)::value;
-      const int k2 = (kt + 2) * BK;
-      constexpr int APP = (CA::NCH + NP - 1) / NP, BPP = (CB::NCH + NP - 1) / NP;
+      const int ST = kt & 1, NS = ST ^ 1;
 #pragma unroll
       for (int pr = 0; pr < NP; ++pr) {
         mfma_pair(fa0, fb0, pr);
@@ -396,49 +425,26 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
         mfma_pair(fa0, fb0, pr);
 #pragma unroll
         for (int r = 0; r < RPP; ++r) read_one(ST, 3, pr * RPP + r, fa1, fb1);
-        if constexpr (HAS1) {
-#pragma unroll
-          for (int c = 0; c < APP; ++c) {
-            const int i = pr * APP + c;
-            if (i < CA::NCH) {
-              ca.template store_chunk<MASKED>(smem + NS * A_REG, i);
-              if constexpr (HAS2 && WK) load_a(k2, i);
-            }
-          }
-#pragma unroll
-          for (int c = 0; c < BPP; ++c) {
-            const int i = pr * BPP + c;
-            if (i < CB::NCH) {
-              cb.template store_chunk<MASKED>(smem + B_OFF + NS * B_REG, i);
-              if constexpr (HAS2 && XK) load_b(k2, i);
-            }
-          }
-        }
         __builtin_amdgcn_sched_barrier(0);
       }
-      constexpr int AH = (CA::NCH + HP - 1) / HP, BH = (CB::NCH + HP - 1) / HP;
 #pragma unroll
       for (int pr = 0; pr < HP; ++pr) {
         mfma_pair(fa1, fb1, pr);
-        if constexpr (HAS2 && !WK) {
-#pragma unroll
-          for (int c = 0; c < AH; ++c)
-            if (pr * AH + c < CA::NCH) load_a(k2, pr * AH + c);
-        }
-        if constexpr (HAS2 && !XK) {
-#pragma unroll
-          for (int c = 0; c < BH; ++c)
-            if (pr * BH + c < CB::NCH) load_b(k2, pr * BH + c);
-        }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (HAS1) wait_vmcnt<0>();
       __syncthreads();
+      const int k2 = (kt + 2) * BK;
 #pragma unroll
       for (int pr = HP; pr < NP; ++pr) {
         mfma_pair(fa1, fb1, pr);
         if constexpr (HAS1) {
 #pragma unroll
           for (int r = 0; r < RPH; ++r) read_one(NS, 0, (pr - HP) * RPH + r, fa0, fb0);
+        }
+        if constexpr (HAS2) {
+#pragma unroll
+          for (int r = 0; r < DPP; ++r) dma(k2, ST, (pr - HP) * DPP + r);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
