@@ -9,6 +9,15 @@
 // (gamma, r, s, lse, labels, positions), tile loads (z, u, dRes, pre), tile
 // reductions (sum of squares, the s statistic, dgamma column sums) and
 // stateful transforms (running max / sum-exp of the cross-entropy).
+//
+// Memory access.  Every tile load and store goes through a raw buffer
+// descriptor based at the wave tile's origin; an access outside the matrix
+// (token >= M or feature >= N) uses an offset beyond the descriptor range,
+// for which the hardware returns zeros (loads) or drops the write (stores).
+// The epilogues are therefore branch-free: a functor first issues all its
+// tile loads (or those of the next 32-token column, for functors that read
+// two tiles), then computes and stores, so load latencies overlap instead of
+// adding up.
 #pragma once
 
 #include "coda_mainloop.hpp"
@@ -16,12 +25,68 @@
 namespace coda {
 
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr uint32_t OOB = 0x80000000u;  // an offset beyond every descriptor range
 
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + fast_exp(-x)); }
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + fast_exp(-x)); }
 
 // Sum over the two lanes (l, l^32) that hold the same token.
 __device__ __forceinline__ float sum_halves(float v) { return v + __shfl_xor(v, 32); }
+
+// A row-major matrix restricted to one wave tile: element (t, f) of the tile
+// (t = token offset, f = feature offset from the wave tile origin).
+template <int ESIZE>
+struct TileView {
+  __amdgpu_buffer_rsrc_t rs;
+  int ld;
+  __device__ __forceinline__ TileView(const void* base, int ld_, int t0, int f0) : ld(ld_) {
+    const char* b = reinterpret_cast<const char*>(base) + ((size_t)t0 * ld_ + f0) * ESIZE;
+    rs = __builtin_amdgcn_make_buffer_rsrc((void*)b, (short)0, 0x7fffffff, 0x00020000);
+  }
+  __device__ __forceinline__ uint32_t off(int t, int f, bool ok) const {
+    return ok ? (uint32_t)(t * ld + f) * (uint32_t)ESIZE : OOB;
+  }
+  __device__ __forceinline__ u32x4 load16(int t, int f, bool ok) const {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off(t, f, ok), 0, 0));
+  }
+  __device__ __forceinline__ void store16(int t, int f, bool ok, u32x4 v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off(t, f, ok), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __device__ __forceinline__ void store8(int t, int f, bool ok, u32x2 v) const {
+    __builtin_amdgcn_raw_buffer_store_b64(v, rs, off(t, f, ok), 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+};
+
+// Lane geometry inside the wave tile.
+struct Lane {
+  int T, F;       // tokens / features remaining from the wave tile origin
+  int lt, hh;
+  __device__ __forceinline__ Lane(const Geom& g) : T(g.T - g.tw0), F(g.F - g.fw0), lt(g.lt), hh(g.hh) {}
+  __device__ __forceinline__ int t(int ci) const { return ci * 32 + lt; }
+  __device__ __forceinline__ int f(int ri, int half) const { return ri * 32 + half * 16 + hh * 8; }
+  __device__ __forceinline__ bool tok(int ci) const { return t(ci) < T; }
+  __device__ __forceinline__ bool ok(int ci, int ri, int half) const { return t(ci) < T && f(ri, half) < F; }
+};
+
+// Vector element loads with the index clamped into range (always valid).
+template <class T_>
+__device__ __forceinline__ T_ vload(const T_* v, int i, int n) { return v[i < n ? i : n - 1]; }
+__device__ __forceinline__ u32x4 vload16_bf16(const uint16_t* v, int i, int n) {
+  return ld16(v + (i < n ? i : n - 8));
+}
+
+// Eight accumulator elements of block (ri, ci), copied from their AGPRs at
+// this point of the program.  Left to itself the register allocator copies
+// all 256 accumulators into VGPRs where the main loop ends, which takes every
+// VGPR and makes the epilogue spill; the explicit per-element reads (volatile,
+// so they keep their place between the stores) avoid that.
+template <int RI, int CI>
+__device__ __forceinline__ void acc8(const f32x16 (&acc)[RI][CI], int ri, int ci, int half, float (&v)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[e]) : "a"(acc[ri][ci][8 * half + e]));
+}
 
 // ---------------------------------------------------------------------------
 // Store-only / row-scale / residual epilogue:  Y = bf16( r_t * acc + res )
@@ -37,27 +102,36 @@ struct EpiLinear {
 
   template <int RI, int CI>
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+    const Lane L(g);
+    const TileView<2> y(Y, ldy, g.tw0, g.fw0);
+    u32x4 rv[CI][RI][2];
+    if constexpr (HAS_RES) {
+      const TileView<2> rz(res, ldres, g.tw0, g.fw0);
+#pragma unroll
+      for (int ci = 0; ci < CI; ++ci)
+#pragma unroll
+        for (int ri = 0; ri < RI; ++ri)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) rv[ci][ri][h] = rz.load16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h));
+    }
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
-      const int t = tok_of(g, ci);
-      if (t >= g.T) continue;
-      const float rs = HAS_R ? r[t] : 1.0f;
+      const float rs = HAS_R ? vload(r, g.tw0 + L.t(ci), g.T) : 1.0f;
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int f = feat_of(g, ri, half);
-          if (f >= g.F) continue;
+        for (int h = 0; h < 2; ++h) {
           float v[8];
+          acc8(acc, ri, ci, h, v);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = acc[ri][ci][8 * half + e] * rs;
+          for (int e = 0; e < 8; ++e) v[e] *= rs;
           if constexpr (HAS_RES) {
             float z[8];
-            unpack8(ld16(res + (size_t)t * ldres + f), z);
+            unpack8(rv[ci][ri][h], z);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] += z[e];
           }
-          st16(Y + (size_t)t * ldy + f, pack8(v));
+          y.store16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h), pack8(v));
         }
     }
   }
@@ -82,53 +156,64 @@ struct EpiResSumsq {
 
   template <int RI, int CI>
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
-    float gm[RI][2][8];
+    const Lane L(g);
+    const TileView<2> uo(U, ldu, g.tw0, g.fw0);
+    u32x4 gv[RI][2];
     if constexpr (HAS_H2) {
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int f = feat_of(g, ri, half);
-          if (f < g.F)
-            unpack8(ld16(gamma + f), gm[ri][half]);
-          else
-#pragma unroll
-            for (int e = 0; e < 8; ++e) gm[ri][half][e] = 0.0f;
-        }
+        for (int h = 0; h < 2; ++h) gv[ri][h] = vload16_bf16(gamma, g.fw0 + L.f(ri, h), g.F);
     }
+    // z is double-buffered per 32-token column (loads of column ci+1 are in
+    // flight while column ci is computed and stored).
+    const TileView<2> zi(z, ldz, g.tw0, g.fw0);
+    u32x4 zv[2][RI][2];
+    auto load_col = [&](int ci, u32x4 (&b)[RI][2]) {
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) b[ri][h] = zi.load16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h));
+    };
+    if constexpr (HAS_Z) load_col(0, zv[0]);
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
-      const int t = tok_of(g, ci);
-      const bool tok_ok = t < g.T;
+      if constexpr (HAS_Z) {
+        if (ci + 1 < CI) load_col(ci + 1, zv[(ci + 1) & 1]);
+      }
       float ss = 0.0f;
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int f = feat_of(g, ri, half);
-          if (!tok_ok || f >= g.F) continue;
+        for (int h = 0; h < 2; ++h) {
+          const bool ok = L.ok(ci, ri, h);
           float v[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = acc[ri][ci][8 * half + e];
+          acc8(acc, ri, ci, h, v);
           if constexpr (HAS_Z) {
             float zz[8];
-            unpack8(ld16(z + (size_t)t * ldz + f), zz);
+            unpack8(zv[ci & 1][ri][h], zz);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] += zz[e];
           }
-          st16(U + (size_t)t * ldu + f, pack8(v));
+          uo.store16(L.t(ci), L.f(ri, h), ok, pack8(v));
+          float sq = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+          for (int e = 0; e < 8; ++e) sq += v[e] * v[e];
+          ss += ok ? sq : 0.0f;
           if constexpr (HAS_H2) {
-            float h[8];
+            float gm[8], hv[8];
+            unpack8(gv[ri][h], gm);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) h[e] = v[e] * gm[ri][half][e];
-            st16(H2 + (size_t)t * ldh + f, pack8(h));
+            for (int e = 0; e < 8; ++e) hv[e] = v[e] * gm[e];
+            const TileView<2> ho(H2, ldh, g.tw0, g.fw0);
+            ho.store16(L.t(ci), L.f(ri, h), ok, pack8(hv));
           }
         }
       if constexpr (HAS_PART) {
         ss = sum_halves(ss);
-        if (g.hh == 0 && tok_ok && g.fw0 < g.F) part[(size_t)t * nparts + g.pf] = ss;
+        const bool w = g.hh == 0 && L.tok(ci) && L.F > 0;
+        const int t = g.tw0 + L.t(ci);
+        if (w) part[(size_t)t * nparts + g.pf] = ss;
       }
     }
   }
@@ -151,48 +236,46 @@ struct EpiRope {
 
   template <int RI, int CI>
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
-    // Per-lane frequencies in revolutions per position: theta^(-2k/hd) / (2 pi).
+    const Lane L(g);
+    const TileView<2> y(Y, ldy, g.tw0, g.fw0);
+    // Per-lane frequencies in revolutions per position: theta^(-2k/hd) / (2 pi);
+    // 0 for pass-through columns (angle 0 rotates by the identity).
     constexpr float INV_2PI = 0.15915494309189535f;
     float fr[RI][2][4];
 #pragma unroll
     for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int f = feat_of(g, ri, half);
+      for (int h = 0; h < 2; ++h) {
+        const int f = g.fw0 + L.f(ri, h);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int k = ((f + 2 * q) % head_dim) >> 1;
-          fr[ri][half][q] = exp2f(-(float)(2 * k) / (float)head_dim * log2_theta) * INV_2PI;
+          const float w = exp2f(-(float)(2 * k) / (float)head_dim * log2_theta) * INV_2PI;
+          fr[ri][h][q] = f < n_rope ? w : 0.0f;
         }
       }
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
-      const int t = tok_of(g, ci);
-      if (t >= g.T) continue;
-      const float rs = HAS_R ? r[t] : 1.0f;
-      const float ps = (float)pos[t];
+      const int t = g.tw0 + L.t(ci);
+      const float rs = HAS_R ? vload(r, t, g.T) : 1.0f;
+      const float ps = (float)vload(pos, t, g.T);
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int f = feat_of(g, ri, half);
-          if (f >= g.F) continue;
+        for (int h = 0; h < 2; ++h) {
           float v[8];
+          acc8(acc, ri, ci, h, v);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = acc[ri][ci][8 * half + e] * rs;
-          if (f < n_rope) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float rev = ps * fr[ri][half][q];
-              rev -= floorf(rev);
-              float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
-              if (INV) sn = -sn;
-              const float a = v[2 * q], b = v[2 * q + 1];
-              v[2 * q] = a * cs - b * sn;
-              v[2 * q + 1] = a * sn + b * cs;
-            }
+          for (int q = 0; q < 4; ++q) {
+            float rev = ps * fr[ri][h][q];
+            rev -= floorf(rev);
+            float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+            if (INV) sn = -sn;
+            const float a = v[2 * q] * rs, b = v[2 * q + 1] * rs;
+            v[2 * q] = a * cs - b * sn;
+            v[2 * q + 1] = a * sn + b * cs;
           }
-          st16(Y + (size_t)t * ldy + f, pack8(v));
+          y.store16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h), pack8(v));
         }
     }
   }
@@ -213,29 +296,31 @@ struct EpiSwiglu {
 
   template <int RI, int CI>
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+    const Lane L(g);
+    const TileView<2> ao(act, ldact, g.tw0, g.fw0 >> 1);
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
-      const int t = tok_of(g, ci);
-      if (t >= g.T) continue;
-      const float rs = HAS_R ? r[t] : 1.0f;
+      const float rs = HAS_R ? vload(r, g.tw0 + L.t(ci), g.T) : 1.0f;
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int f = feat_of(g, ri, half);
-          if (f >= g.F) continue;
+        for (int h = 0; h < 2; ++h) {
+          const bool ok = L.ok(ci, ri, h);
           float v[8];
+          acc8(acc, ri, ci, h, v);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = acc[ri][ci][8 * half + e] * rs;
+          for (int e = 0; e < 8; ++e) v[e] *= rs;
           float a[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float gg = v[2 * q], uu = v[2 * q + 1];
             a[q] = gg * sigmoidf_(gg) * uu;
           }
-          *reinterpret_cast<u32x2*>(act + (size_t)t * ldact + (f >> 1)) =
-              (u32x2){pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-          if constexpr (HAS_PRE) st16(pre + (size_t)t * ldp + f, pack8(v));
+          ao.store8(L.t(ci), L.f(ri, h) >> 1, ok, (u32x2){pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])});
+          if constexpr (HAS_PRE) {
+            const TileView<2> po(pre, ldp, g.tw0, g.fw0);
+            po.store16(L.t(ci), L.f(ri, h), ok, pack8(v));
+          }
         }
     }
   }
@@ -255,41 +340,46 @@ struct EpiCE {
 
   template <int RI, int CI>
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+    const Lane L(g);
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
-      const int t = tok_of(g, ci);
-      const bool tok_ok = t < g.T;
-      const int label = tok_ok ? labels[t] : -1;
+      const int t = g.tw0 + L.t(ci);
+      const bool tok_ok = L.tok(ci);
+      // feature index of the label relative to this lane's first feature
+      const int label = tok_ok ? vload(labels, t, g.T) - g.fw0 : -1;
+      float l[RI][2][8];
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc8(acc, ri, ci, h, l[ri][h]);
       float m = -INFINITY;
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int f = feat_of(g, ri, half);
-          if (f >= g.F) continue;
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) m = fmaxf(m, acc[ri][ci][8 * half + e]);
-        }
-      float s = 0.0f;
+          for (int e = 0; e < 8; ++e) m = (L.f(ri, h) + e < L.F) ? fmaxf(m, l[ri][h][e]) : m;
+      float s = 0.0f, tv = 0.0f;
+      bool hit = false;
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int f = feat_of(g, ri, half);
-          if (f >= g.F) continue;
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float l = acc[ri][ci][8 * half + e];
-            s += fast_exp(l - m);
-            if (label == f + e) tgt[t] = l;
+            const int fe = L.f(ri, h) + e;
+            s += (fe < L.F) ? fast_exp(l[ri][h][e] - m) : 0.0f;
+            const bool is = label == fe;
+            tv = is ? l[ri][h][e] : tv;
+            hit = hit || is;
           }
-        }
+      if (hit) tgt[t] = tv;
       // merge the two half-wave states of this token
       const float m2 = __shfl_xor(m, 32), s2 = __shfl_xor(s, 32);
       const float mm = fmaxf(m, m2);
       const float st = (m == -INFINITY ? 0.0f : s * fast_exp(m - mm)) +
                        (m2 == -INFINITY ? 0.0f : s2 * fast_exp(m2 - mm));
-      if (g.hh == 0 && tok_ok && g.fw0 < g.F) {
+      if (g.hh == 0 && tok_ok && L.F > 0) {
         part_m[(size_t)t * nparts + g.pf] = mm;
         part_s[(size_t)t * nparts + g.pf] = st;
       }
@@ -310,25 +400,25 @@ struct EpiCEBwd {
 
   template <int RI, int CI>
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+    const Lane L(g);
+    const TileView<2> d(D, ldd, g.tw0, g.fw0);
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
-      const int t = tok_of(g, ci);
-      if (t >= g.T) continue;
-      const int label = labels[t];
-      const float L = lse[t];
+      const int t = g.tw0 + L.t(ci);
+      const int label = vload(labels, t, g.T) - g.fw0;
+      const float Lse = vload(lse, t, g.T);
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int f = feat_of(g, ri, half);
-          if (f >= g.F) continue;
+        for (int h = 0; h < 2; ++h) {
           float v[8];
+          acc8(acc, ri, ci, h, v);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float pr = fast_exp(acc[ri][ci][8 * half + e] - L);
-            v[e] = (pr - (label == f + e ? 1.0f : 0.0f)) * scale;
+            const float pr = fast_exp(v[e] - Lse);
+            v[e] = (pr - (label == L.f(ri, h) + e ? 1.0f : 0.0f)) * scale;
           }
-          st16(D + (size_t)t * ldd + f, pack8(v));
+          d.store16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h), pack8(v));
         }
     }
   }
@@ -350,38 +440,56 @@ struct EpiSwigluBwd {
 
   template <int RI, int CI>
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+    const Lane L(g);
+    // The feature space of this GEMM is F (da_j); pre/dpre columns are 2j, 2j+1.
+    const TileView<2> pi(pre, ldp, g.tw0, 2 * g.fw0);
+    const TileView<2> po(dpre, lddp, g.tw0, 2 * g.fw0);
+    u32x4 pv[2][RI][2][2];
+    auto load_col = [&](int ci, u32x4 (&b)[RI][2][2]) {
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) b[ri][h][c] = pi.load16(L.t(ci), 2 * L.f(ri, h) + 8 * c, L.ok(ci, ri, h));
+    };
+    load_col(0, pv[0]);
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
-      const int t = tok_of(g, ci);
-      const bool tok_ok = t < g.T;
+      if (ci + 1 < CI) load_col(ci + 1, pv[(ci + 1) & 1]);
       float ss = 0.0f;
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int f = feat_of(g, ri, half);
-          if (!tok_ok || f >= g.F) continue;
+        for (int h = 0; h < 2; ++h) {
+          const bool ok = L.ok(ci, ri, h);
+          float dav[8];
+          acc8(acc, ri, ci, h, dav);
 #pragma unroll
           for (int c = 0; c < 2; ++c) {  // two 16-byte chunks = 4 pairs each
-            float pv[8], out[8];
-            unpack8(ld16(pre + (size_t)t * ldp + 2 * f + 8 * c), pv);
+            float pvv[8], out[8];
+            unpack8(pv[ci & 1][ri][h][c], pvv);
+            float part = 0.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float da = acc[ri][ci][8 * half + 4 * c + q];
-              const float gg = pv[2 * q], uu = pv[2 * q + 1];
+              const float da = dav[4 * c + q];
+              const float gg = pvv[2 * q], uu = pvv[2 * q + 1];
               const float sg = sigmoidf_(gg);
               const float dg = da * uu * sg * (1.0f + gg * (1.0f - sg));
               const float du = da * gg * sg;
               out[2 * q] = dg;
               out[2 * q + 1] = du;
-              ss += dg * gg + du * uu;
+              part += dg * gg + du * uu;
             }
-            st16(dpre + (size_t)t * lddp + 2 * f + 8 * c, pack8(out));
+            ss += ok ? part : 0.0f;
+            po.store16(L.t(ci), 2 * L.f(ri, h) + 8 * c, ok, pack8(out));
           }
         }
       if constexpr (HAS_SPART) {
         ss = sum_halves(ss);
-        if (g.hh == 0 && tok_ok && g.fw0 < g.F) spart[(size_t)t * nparts + g.pf] = ss;
+        const bool w = g.hh == 0 && L.tok(ci) && L.F > 0;
+        const int t = g.tw0 + L.t(ci);
+        if (w) spart[(size_t)t * nparts + g.pf] = ss;
       }
     }
   }
@@ -411,81 +519,95 @@ struct EpiRowscaleBwd {
   template <int RI, int CI>
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
     static_assert(CI * 32 == WAVE_T, "column partials assume 128-token wave tiles");
-    float gm[RI][2][8];
-    float col[RI * 16];
-#pragma unroll
-    for (int i = 0; i < RI * 16; ++i) col[i] = 0.0f;
-#pragma unroll
-    for (int ri = 0; ri < RI; ++ri)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int f = feat_of(g, ri, half);
-        if (f < g.F)
-          unpack8(ld16(gamma + f), gm[ri][half]);
-        else
-#pragma unroll
-          for (int e = 0; e < 8; ++e) gm[ri][half][e] = 0.0f;
-      }
+    const Lane L(g);
+    const TileView<2> ui(u, ldu, g.tw0, g.fw0);
+    const TileView<2> ri_(dres, ldr, g.tw0, g.fw0);
+    const TileView<2> duo(du, lddu, g.tw0, g.fw0);
+    const TileView<2> n2o(n2, ldn, g.tw0, g.fw0);
+    // Per-token factors of the four 32-token columns.
+    float rt[CI], c2[CI];
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
-      const int t = tok_of(g, ci);
-      if (t >= g.T) continue;
-      const float rt = r[t], st = s[t];
-      const float c2 = rt * rt * st;
+      const int t = g.tw0 + L.t(ci);
+      rt[ci] = L.tok(ci) ? vload(r, t, g.T) : 0.0f;
+      c2[ci] = rt[ci] * rt[ci] * vload(s, t, g.T);
+    }
+    // Feature-block order (ri outer): the dgamma column sums of one 32-feature
+    // block are finished and reduced over the tokens before the next block, so
+    // only 16 of them are live at a time.
+    float gsum[RI];
 #pragma unroll
-      for (int ri = 0; ri < RI; ++ri)
+    for (int ri = 0; ri < RI; ++ri) {
+      u32x4 gv[2], uv[CI][2], rv[CI][2];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int f = feat_of(g, ri, half);
-          if (f >= g.F) continue;
-          float uv[8], o[8];
-          unpack8(ld16(u + (size_t)t * ldu + f), uv);
+      for (int h = 0; h < 2; ++h) gv[h] = vload16_bf16(gamma, g.fw0 + L.f(ri, h), g.F);
+#pragma unroll
+      for (int ci = 0; ci < CI; ++ci)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uv[ci][h] = ui.load16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h));
+          if constexpr (HAS_RES) rv[ci][h] = ri_.load16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h));
+        }
+      float col[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) col[i] = 0.0f;
+#pragma unroll
+      for (int ci = 0; ci < CI; ++ci)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bool ok = L.ok(ci, ri, h);
+          float uvv[8], o[8], gm[8], Gv[8];
+          acc8(acc, ri, ci, h, Gv);
+          unpack8(uv[ci][h], uvv);
+          unpack8(gv[h], gm);
           if constexpr (HAS_RES) {
-            unpack8(ld16(dres + (size_t)t * ldr + f), o);
+            unpack8(rv[ci][h], o);
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = 0.0f;
           }
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float G = acc[ri][ci][8 * half + e];
-            o[e] += rt * (G * gm[ri][half][e]) - c2 * uv[e];
-            col[ri * 16 + half * 8 + e] += rt * G * uv[e];
+            const float G = Gv[e];
+            o[e] += rt[ci] * (G * gm[e]) - c2[ci] * uvv[e];
+            col[h * 8 + e] += rt[ci] * G * uvv[e];  // rt = 0 and u = 0 outside the matrix
           }
-          st16(du + (size_t)t * lddu + f, pack8(o));
+          duo.store16(L.t(ci), L.f(ri, h), ok, pack8(o));
           if constexpr (HAS_N2) {
             float nv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) nv[e] = rt * uv[e] * gm[ri][half][e];
-            st16(n2 + (size_t)t * ldn + f, pack8(nv));
+            for (int e = 0; e < 8; ++e) nv[e] = rt[ci] * uvv[e] * gm[e];
+            n2o.store16(L.t(ci), L.f(ri, h), ok, pack8(nv));
           }
         }
+      if constexpr (HAS_GPART) {
+        // Transpose-reduce the 16 column sums over the 32 token lanes: halving
+        // at lane distances 16, 8, 4, 2 leaves entry lt/2 (summed over 16
+        // lanes) in lane lt; the last step adds the neighbour at distance 1.
+#pragma unroll
+        for (int step = 0; step < 4; ++step) {
+          const int mask = 16 >> step;
+          const int n = 16 >> step;
+          const bool upper = (g.lt & mask) != 0;
+#pragma unroll
+          for (int i = 0; i < n / 2; ++i) {
+            const float keep = upper ? col[i + n / 2] : col[i];
+            const float send = upper ? col[i] : col[i + n / 2];
+            col[i] = keep + __shfl_xor(send, mask);
+          }
+        }
+        gsum[ri] = col[0] + __shfl_xor(col[0], 1);
+      }
     }
     if constexpr (HAS_GPART) {
-      // Transpose-reduce the RI*16 column sums over the 32 token lanes: after
-      // halving at lane distances 16, 8, 4, 2, 1 lane lt holds the sums of
-      // entries 2*lt and 2*lt + 1.
-      constexpr int N0 = RI * 16;
-      static_assert(N0 == 64, "butterfly assumes 64 column sums per lane");
+      // Lane lt (even) writes entry lt/2 = 8 half + e of each feature block.
+      const int idx = g.lt >> 1;
+      const TileView<4> gp(gpart, dcols, g.pt, g.fw0);
 #pragma unroll
-      for (int step = 0; step < 5; ++step) {
-        const int mask = 16 >> step;
-        const int n = N0 >> step;
-        const bool upper = (g.lt & mask) != 0;
-#pragma unroll
-        for (int i = 0; i < n / 2; ++i) {
-          const float keep = upper ? col[i + n / 2] : col[i];
-          const float send = upper ? col[i] : col[i + n / 2];
-          col[i] = keep + __shfl_xor(send, mask);
-        }
-      }
-      if (g.tw0 >= g.T) return;  // no token of this wave tile exists
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int idx = 2 * g.lt + j;
-        const int ri = idx >> 4, half = (idx >> 3) & 1, e = idx & 7;
-        const int f = feat_of(g, ri, half) + e;
-        if (f < g.F) gpart[(size_t)g.pt * dcols + f] = col[j];
+      for (int ri = 0; ri < RI; ++ri) {
+        const int f = L.f(ri, idx >> 3) + (idx & 7);
+        const bool ok = L.T > 0 && f < L.F && (g.lt & 1) == 0;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gsum[ri]), gp.rs, gp.off(0, f, ok), 0, 0);
       }
     }
   }
@@ -501,25 +623,41 @@ struct EpiF32 {
 
   template <int RI, int CI>
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
-#pragma unroll
-    for (int ci = 0; ci < CI; ++ci) {
-      const int t = tok_of(g, ci);
-      if (t >= g.T) continue;
+    const Lane L(g);
+    const TileView<4> o(out, ld, g.tw0, g.fw0);
+    u32x4 prev[2][RI][2][2];
+    auto load_col = [&](int ci, u32x4 (&b)[RI][2][2]) {
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int f = feat_of(g, ri, half);
-          if (f >= g.F) continue;
-          float* o = out + (size_t)t * ld + f;
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) b[ri][h][c] = o.load16(L.t(ci), L.f(ri, h) + 4 * c, L.ok(ci, ri, h));
+    };
+    if constexpr (ACCUM) load_col(0, prev[0]);
+#pragma unroll
+    for (int ci = 0; ci < CI; ++ci) {
+      if constexpr (ACCUM) {
+        if (ci + 1 < CI) load_col(ci + 1, prev[(ci + 1) & 1]);
+      }
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            f32x4 v = {acc[ri][ci][8 * half + 4 * c + 0], acc[ri][ci][8 * half + 4 * c + 1],
-                       acc[ri][ci][8 * half + 4 * c + 2], acc[ri][ci][8 * half + 4 * c + 3]};
-            if constexpr (ACCUM) v += *reinterpret_cast<const f32x4*>(o + 4 * c);
-            *reinterpret_cast<f32x4*>(o + 4 * c) = v;
+            f32x4 v;
+            if constexpr (ACCUM) {
+              float a[8];
+              acc8(acc, ri, ci, h, a);
+              v = (f32x4){a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]} +
+                  __builtin_bit_cast(f32x4, prev[ci & 1][ri][h][c]);
+            } else {  // stored straight from the accumulator registers
+              v = (f32x4){acc[ri][ci][8 * h + 4 * c + 0], acc[ri][ci][8 * h + 4 * c + 1],
+                          acc[ri][ci][8 * h + 4 * c + 2], acc[ri][ci][8 * h + 4 * c + 3]};
+            }
+            o.store16(L.t(ci), L.f(ri, h) + 4 * c, L.ok(ci, ri, h), __builtin_bit_cast(u32x4, v));
           }
-        }
     }
   }
 };

@@ -462,6 +462,10 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
   else
     mainloop(std::true_type{});
 
+  // The epilogues copy accumulators out of their AGPRs with inline asm, which
+  // the compiler's hazard check does not see: 24 wait states cover the
+  // longest MFMA-write to VALU-read distance the ISA requires.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
   Geom g;
   g.fw0 = f0 + wf * WF;
   g.tw0 = t0 + wt * WT;

@@ -97,3 +97,20 @@ def test_fused_validation(L):
                                 128, None, 0, 16, 128, 64, None) == 6
     # col_reduce: mparts < 1
     assert L.coda_col_reduce(A16, 0, 64, A16b, None) == 2
+
+
+def test_no_kernel_spills():
+    """Every kernel of the built library runs without scratch memory (the build
+    records the compiler's resource report next to the library)."""
+    import json
+    import os
+    from gemm_epilogue_transformer_mainloop_amd import build as B
+    if not os.path.exists(B.RESOURCES):
+        pytest.skip("library not built with the resource report")
+    res = json.load(open(B.RESOURCES))
+    gemm = {k: v for k, v in res.items() if "gemm_epi_kernel" in k}
+    assert len(gemm) >= 20
+    for name, v in res.items():
+        assert v["scratch"] == 0 and v["vgpr_spill"] == 0, name
+    # the main loop holds the 128x128 wave tile in the 256 accumulation registers
+    assert all(v["agprs"] == 256 for v in gemm.values())
