@@ -311,7 +311,10 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
   constexpr int NRB = XK ? CI : 2 * CI;
   constexpr int NRD = NRA + NRB;
   constexpr int RPP = (NRD + NP - 1) / NP;
-  constexpr int HP = NP / 2;                // pairs before the barrier in step 3
+  // Pairs of step 3 before the barrier.  0 (barrier at the start of step 3,
+  // once the step-3 fragments are read) lets the DMA of k-tile kt+2 spread
+  // over all 8 pairs: measured 7% fewer cycles per k-tile than 4.
+  constexpr int HP = 0;
   constexpr int RPH = (NRD + (NP - HP) - 1) / (NP - HP);
   constexpr int NDMA = OA::NCH + OB::NCH;
   constexpr int DPP = (NDMA + (NP - HP) - 1) / (NP - HP);
@@ -400,9 +403,9 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
 
     // One k-tile: four k-steps of NP MFMA pairs, each pair carrying the
     // fragment reads of the next k-step (other register set).  In step 3,
-    // after half the MFMAs: wait for k-tile kt+1's DMA, barrier, then the
-    // first fragment reads of k-tile kt+1 and the DMA of k-tile kt+2 into
-    // the stage k-tile kt has released.  sched_barrier fences keep the order.
+    // after HP pairs: wait for k-tile kt+1's DMA, barrier, then the first
+    // fragment reads of k-tile kt+1 and the DMA of k-tile kt+2 into the stage
+    // k-tile kt has released.  sched_barrier fences keep the order.
     auto ktile = [&](int kt, auto has1_c, auto has2_c) {
       constexpr bool HAS1 = decltype(has1_c)::value, HAS2 = decltype(has2_c)::value;
       const int ST = kt & 1, NS = ST ^ 1;
