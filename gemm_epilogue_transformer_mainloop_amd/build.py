@@ -28,7 +28,7 @@ LIB = os.path.join(HERE, "libcoda.so")
 RESOURCES = os.path.join(HERE, "libcoda.resources.json")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["coda_api.hip", "coda_baseline.hip"]
+SOURCES = ["coda_api.hip", "coda_unfused.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

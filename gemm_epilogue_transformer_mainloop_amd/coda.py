@@ -18,7 +18,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcoda.so")
-HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "coda.h")
+INCLUDE_DIR = os.path.join(os.path.dirname(_HERE), "include")
+HEADER_PATHS = [os.path.join(INCLUDE_DIR, h) for h in ("coda.h", "coda_unfused.h")]
 
 _lib = None
 
@@ -50,6 +51,16 @@ _SIGS = {
     "coda_gemm_res_sumsq_bwd": (I, [P, I, P, I, P, I, P, I, P, I, P, I, I, I, I, P]),
     "coda_gemm_wgrad": (I, [P, I, P, I, P, I, I, I, I, I, P]),
     "coda_lmhead_ce_bwd": (I, [P, I, P, I, P, P, F, P, I, P, I, P, SZ, I, I, I, P]),
+    # include/coda_unfused.h
+    "coda_unfused_add": (I, [P, I, P, I, P, I, I, I, P]),
+    "coda_unfused_add_rmsnorm": (I, [P, I, P, I, P, F, P, I, P, I, P, I, I, P]),
+    "coda_unfused_rope": (I, [P, I, P, F, I, I, I, I, I, P]),
+    "coda_unfused_swiglu": (I, [P, I, P, I, I, I, P]),
+    "coda_unfused_swiglu_bwd": (I, [P, I, P, I, P, I, I, I, P]),
+    "coda_unfused_rmsnorm_bwd_parts": (I, [I]),
+    "coda_unfused_rmsnorm_bwd": (I, [P, I, P, I, P, P, P, I, P, I, P, I, I, P]),
+    "coda_unfused_cross_entropy": (I, [P, I, P, P, P, P, I, I, P]),
+    "coda_unfused_cross_entropy_bwd": (I, [P, I, P, P, F, P, I, I, I, P]),
 }
 
 STATUS = {0: "CODA_OK", 1: "CODA_ERR_NULL", 2: "CODA_ERR_SHAPE", 3: "CODA_ERR_ALIGN",
@@ -78,11 +89,14 @@ def lib():
 
 
 def header_functions():
-    """Names of the functions include/coda.h declares."""
-    with open(HEADER_PATH) as f:
-        src = f.read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(coda_[a-z0-9_]+)\s*\(", src)))
+    """Names of the functions include/coda.h and include/coda_unfused.h declare."""
+    names = set()
+    for path in HEADER_PATHS:
+        with open(path) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names.update(re.findall(r"\b(coda_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def status_str(s: int) -> str:
@@ -329,3 +343,91 @@ def coda_lmhead_ce_bwd(H, W, labels, lse, grad_scale: float, dH=None, dW=None, w
           ctypes.c_float(grad_scale), _ptr(dH), _ld(dH), _ptr(dW), _ld(dW), _ptr(ws), ws.numel() * ws.element_size(),
           M, V, d, _stream())
     return dH, dW
+
+
+# ----------------------------------------------------------------------------
+# unfused baseline (include/coda_unfused.h)
+# ----------------------------------------------------------------------------
+
+
+def coda_unfused_add(A, B, C=None):
+    M, N = A.shape
+    if C is None:
+        C = _empty((M, N), torch.bfloat16, A)
+    _call("coda_unfused_add", _ptr(A), _ld(A), _ptr(B), _ld(B), _ptr(C), _ld(C), M, N, _stream())
+    return C
+
+
+def coda_unfused_add_rmsnorm(Y, Z, gamma, eps: float, U=None, N2=None, r=None):
+    M, d = Y.shape
+    if U is None:
+        U = _empty((M, d), torch.bfloat16, Y)
+    if N2 is None:
+        N2 = _empty((M, d), torch.bfloat16, Y)
+    if r is None:
+        r = _empty((M,), torch.float32, Y)
+    _call("coda_unfused_add_rmsnorm", _ptr(Y), _ld(Y), _ptr(Z), _ld(Z), _ptr(gamma), ctypes.c_float(eps), _ptr(U),
+          _ld(U), _ptr(N2), _ld(N2), _ptr(r), M, d, _stream())
+    return U, N2, r
+
+
+def coda_unfused_rope(Y, pos, theta: float, head_dim: int, n_rope: int, inverse: bool = False):
+    M, N = Y.shape
+    _call("coda_unfused_rope", _ptr(Y), _ld(Y), _ptr(pos), ctypes.c_float(theta), head_dim, n_rope, int(inverse),
+          M, N, _stream())
+    return Y
+
+
+def coda_unfused_swiglu(Pre, Act=None):
+    M, F2 = Pre.shape
+    F = F2 // 2
+    if Act is None:
+        Act = _empty((M, F), torch.bfloat16, Pre)
+    _call("coda_unfused_swiglu", _ptr(Pre), _ld(Pre), _ptr(Act), _ld(Act), M, F, _stream())
+    return Act
+
+
+def coda_unfused_swiglu_bwd(dA, Pre, dPre=None):
+    M, F = dA.shape
+    if dPre is None:
+        dPre = _empty((M, 2 * F), torch.bfloat16, dA)
+    _call("coda_unfused_swiglu_bwd", _ptr(dA), _ld(dA), _ptr(Pre), _ld(Pre), _ptr(dPre), _ld(dPre), M, F, _stream())
+    return dPre
+
+
+def coda_unfused_rmsnorm_bwd_parts(M: int) -> int:
+    return int(lib().coda_unfused_rmsnorm_bwd_parts(M))
+
+
+def coda_unfused_rmsnorm_bwd(G, U, gamma, r, dRes=None, dU=None, gpart=None, want_gpart=True):
+    M, d = G.shape
+    if dU is None:
+        dU = _empty((M, d), torch.bfloat16, G)
+    if gpart is None and want_gpart:
+        gpart = _empty((coda_unfused_rmsnorm_bwd_parts(M), d), torch.float32, G)
+    _dense(gpart, "gpart")
+    _call("coda_unfused_rmsnorm_bwd", _ptr(G), _ld(G), _ptr(U), _ld(U), _ptr(gamma), _ptr(r), _ptr(dRes), _ld(dRes),
+          _ptr(dU), _ld(dU), _ptr(gpart), M, d, _stream())
+    return dU, gpart
+
+
+def coda_unfused_cross_entropy(L, labels, lse=None, loss_row=None, loss_mean=None):
+    M, V = L.shape
+    if lse is None:
+        lse = _empty((M,), torch.float32, L)
+    if loss_row is None:
+        loss_row = _empty((M,), torch.float32, L)
+    if loss_mean is None:
+        loss_mean = _empty((1,), torch.float32, L)
+    _call("coda_unfused_cross_entropy", _ptr(L), _ld(L), _ptr(labels), _ptr(lse), _ptr(loss_row), _ptr(loss_mean),
+          M, V, _stream())
+    return lse, loss_row, loss_mean
+
+
+def coda_unfused_cross_entropy_bwd(L, labels, lse, grad_scale: float, D=None):
+    M, V = L.shape
+    if D is None:
+        D = _empty((M, V), torch.bfloat16, L)
+    _call("coda_unfused_cross_entropy_bwd", _ptr(L), _ld(L), _ptr(labels), _ptr(lse), ctypes.c_float(grad_scale),
+          _ptr(D), _ld(D), M, V, _stream())
+    return D

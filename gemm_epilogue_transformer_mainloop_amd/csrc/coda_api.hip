@@ -12,8 +12,10 @@
 
 #include "../../include/coda.h"
 #include "coda_epilogues.hpp"
+#include "coda_host.hpp"
 
 using namespace coda;
+using namespace coda_host;
 
 namespace {
 
@@ -86,74 +88,6 @@ __global__ void __launch_bounds__(1024) mean_kernel(const float* __restrict__ x,
   }
   if (threadIdx.x == 0) out[0] = sh[0] / (float)M;
 }
-
-// ---------------------------------------------------------------------------
-// Validation helpers
-// ---------------------------------------------------------------------------
-
-inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-struct Check {
-  coda_status st = CODA_OK;
-  void need(const void* p) {
-    if (st == CODA_OK && p == nullptr) st = CODA_ERR_NULL;
-  }
-  // A bf16 matrix of `rows` x `cols`, leading dimension ld (NULL allowed when
-  // optional or when it has no rows).
-  void bmat(const void* p, int ld, int cols, bool required = true, int rows = 1) {
-    if (st != CODA_OK) return;
-    if (p == nullptr) {
-      if (required && rows > 0) st = CODA_ERR_NULL;
-      return;
-    }
-    if (ld < cols || ld <= 0) { st = CODA_ERR_SHAPE; return; }
-    if (!al16(p) || (ld % 8) != 0) st = CODA_ERR_ALIGN;
-  }
-  void fmat(const void* p, int ld, int cols, bool required = true, int rows = 1) {
-    if (st != CODA_OK) return;
-    if (p == nullptr) {
-      if (required && rows > 0) st = CODA_ERR_NULL;
-      return;
-    }
-    if (ld < cols || ld <= 0) { st = CODA_ERR_SHAPE; return; }
-    if (!al16(p) || (ld % 4) != 0) st = CODA_ERR_ALIGN;
-  }
-  void vec(const void* p, bool required = true, bool aligned16 = false, int n = 1) {
-    if (st != CODA_OK) return;
-    if (p == nullptr) {
-      if (required && n > 0) st = CODA_ERR_NULL;
-      return;
-    }
-    if (aligned16 && !al16(p)) st = CODA_ERR_ALIGN;
-  }
-  void shape(bool ok) {
-    if (st == CODA_OK && !ok) st = CODA_ERR_SHAPE;
-  }
-  void unsupported(bool ok) {
-    if (st == CODA_OK && !ok) st = CODA_ERR_UNSUPPORTED;
-  }
-};
-
-// One gfx950 check per device, cached (architecture never changes).
-std::atomic<int> g_arch_ok[64];
-
-coda_status device_ok() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return CODA_ERR_HIP;
-  if (dev < 0 || dev >= 64) return CODA_ERR_UNSUPPORTED;
-  int v = g_arch_ok[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return CODA_ERR_HIP;
-    v = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
-    g_arch_ok[dev].store(v, std::memory_order_relaxed);
-  }
-  return v == 1 ? CODA_OK : CODA_ERR_UNSUPPORTED;
-}
-
-coda_status launched() { return hipGetLastError() == hipSuccess ? CODA_OK : CODA_ERR_HIP; }
-
-inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // Launch one fused GEMM: features F (output columns), tokens T (output rows).
 template <bool WK, bool XK, int BT = 256, class Epi>

@@ -298,14 +298,16 @@ struct EpiSwiglu {
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
     const Lane L(g);
     const TileView<2> ao(act, ldact, g.tw0, g.fw0 >> 1);
+    const TileView<2> po(pre, ldp, g.tw0, g.fw0);
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
       const float rs = HAS_R ? vload(r, g.tw0 + L.t(ci), g.T) : 1.0f;
 #pragma unroll
-      for (int ri = 0; ri < RI; ++ri)
+      for (int ri = 0; ri < RI; ++ri) {
+        // a-columns of this lane: 16 ri + 8 h + 4 hh + q (q = 0..3) for half h
+        u32x2 ah[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const bool ok = L.ok(ci, ri, h);
           float v[8];
           acc8(acc, ri, ci, h, v);
 #pragma unroll
@@ -316,12 +318,23 @@ struct EpiSwiglu {
             const float gg = v[2 * q], uu = v[2 * q + 1];
             a[q] = gg * sigmoidf_(gg) * uu;
           }
-          ao.store8(L.t(ci), L.f(ri, h) >> 1, ok, (u32x2){pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])});
-          if constexpr (HAS_PRE) {
-            const TileView<2> po(pre, ldp, g.tw0, g.fw0);
-            po.store16(L.t(ci), L.f(ri, h), ok, pack8(v));
-          }
+          ah[h] = (u32x2){pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+          if constexpr (HAS_PRE) po.store16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h), pack8(v));
         }
+        // Exchange with lane l ^ 32 so that each lane holds 8 consecutive
+        // a-columns (16 ri + 8 hh + 0..7) and writes them with one 16-byte store.
+        const u32x2 give = g.hh ? ah[0] : ah[1];
+        const u32x2 got = {(uint32_t)__shfl_xor((int)give[0], 32), (uint32_t)__shfl_xor((int)give[1], 32)};
+        const u32x4 out = g.hh ? (u32x4){got[0], got[1], ah[1][0], ah[1][1]}
+                               : (u32x4){ah[0][0], ah[0][1], got[0], got[1]};
+        // The 16 features behind this store are all valid, or (F % 8 == 4 at
+        // the right edge) only the first 8: then the low 8 bytes are stored.
+        const int fb = ri * 32 + g.hh * 16;
+        const bool full = L.tok(ci) && fb + 16 <= L.F;
+        const bool half = L.tok(ci) && fb + 8 <= L.F && !full;
+        ao.store16(L.t(ci), ri * 16 + g.hh * 8, full, out);
+        ao.store8(L.t(ci), ri * 16 + g.hh * 8, half, (u32x2){out[0], out[1]});
+      }
     }
   }
 };

@@ -1,5 +1,6 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
-include/coda.h declares, and rejects bad arguments before any device call."""
+include/coda.h and include/coda_unfused.h declare, and rejects bad arguments
+before any device call."""
 
 import ctypes
 import os
@@ -97,6 +98,37 @@ def test_fused_validation(L):
                                 128, None, 0, 16, 128, 64, None) == 6
     # col_reduce: mparts < 1
     assert L.coda_col_reduce(A16, 0, 64, A16b, None) == 2
+
+
+def test_unfused_validation(L):
+    F = ctypes.c_float
+    assert coda.coda_unfused_rmsnorm_bwd_parts(8192) == 512
+    assert coda.coda_unfused_rmsnorm_bwd_parts(17) == 2
+    assert coda.coda_unfused_rmsnorm_bwd_parts(0) == 0
+    # add: N % 8
+    assert L.coda_unfused_add(A16, 64, A16b, 64, A16c, 64, 16, 60, None) == 2
+    # add_rmsnorm: d too wide for one workgroup per row
+    assert L.coda_unfused_add_rmsnorm(A16, 16384, None, 0, A16b, F(1e-6), A16c, 16384, A16, 16384, A16b,
+                                      4, 16384, None) == 4
+    # add_rmsnorm: NULL r
+    assert L.coda_unfused_add_rmsnorm(A16, 64, None, 0, A16b, F(1e-6), A16c, 64, A16, 64, None, 4, 64,
+                                      None) == 1
+    # rope: n_rope beyond N, odd head_dim
+    assert L.coda_unfused_rope(A16, 64, A16b, F(1e4), 64, 128, 0, 4, 64, None) == 4
+    assert L.coda_unfused_rope(A16, 64, A16b, F(1e4), 7, 0, 0, 4, 64, None) == 4
+    # swiglu: ldp < 2F; misaligned act
+    assert L.coda_unfused_swiglu(A16, 64, A16b, 64, 4, 64, None) == 2
+    assert L.coda_unfused_swiglu(A16, 128, MIS, 64, 4, 64, None) == 3
+    # swiglu_bwd: NULL pre
+    assert L.coda_unfused_swiglu_bwd(A16, 64, None, 128, A16b, 128, 4, 64, None) == 1
+    # rmsnorm_bwd: misaligned gpart
+    assert L.coda_unfused_rmsnorm_bwd(A16, 64, A16b, 64, A16c, A16, None, 0, A16b, 64, MIS, 4, 64,
+                                      None) == 3
+    # cross entropy: V % 8, ld < V
+    assert L.coda_unfused_cross_entropy(A16, 64, A16b, A16c, A16, None, 4, 60, None) == 2
+    assert L.coda_unfused_cross_entropy_bwd(A16, 32, A16b, A16c, F(1.0), A16, 64, 4, 64, None) == 2
+    # empty M: no-op
+    assert L.coda_unfused_cross_entropy(A16, 64, A16b, A16c, A16, None, 0, 64, None) == 0
 
 
 def test_no_kernel_spills():
