@@ -76,6 +76,14 @@ class OpTimer:
     def mean_ms(self):
         return {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in self.ev.items()}
 
+    def stats_ms(self):
+        """Per op: (mean, median, min) over the recorded launches."""
+        out = {}
+        for k, v in self.ev.items():
+            t = [s.elapsed_time(e) for s, e in v]
+            out[k] = (float(np.mean(t)), float(np.median(t)), float(np.min(t)))
+        return out
+
 
 def time_fn(torch, fn, iters=20, warmup=5):
     for _ in range(warmup):
@@ -134,6 +142,59 @@ def make_c2_step(torch, coda, T, dims, eps):
                                                  Y=buf["Yr"]))
 
     return step, buf, n_rope
+
+
+def make_c2_unfused_step(torch, coda, T, dims, eps, n_rope):
+    """The same block as the conventional sequence: plain GEMM, standalone
+    residual-add + RMSNorm, plain GEMMs, standalone RoPE."""
+    M, d, K, N, NR = dims
+    bf = torch.bfloat16
+    buf = {
+        "Y0": torch.empty(M, d, dtype=bf, device="cuda"),
+        "U": torch.empty(M, d, dtype=bf, device="cuda"),
+        "N2": torch.empty(M, d, dtype=bf, device="cuda"),
+        "r": torch.empty(M, dtype=torch.float32, device="cuda"),
+        "Y": torch.empty(M, N, dtype=bf, device="cuda"),
+        "Yr": torch.empty(M, NR, dtype=bf, device="cuda"),
+    }
+
+    def step(tm=None):
+        run = tm.run if tm is not None else (lambda n, f: f())
+        run("gemm0", lambda: coda.coda_gemm(T["x"], T["W0"], buf["Y0"]))
+        run("add_rmsnorm", lambda: coda.coda_unfused_add_rmsnorm(buf["Y0"], T["z"], T["gamma"], eps, U=buf["U"],
+                                                                 N2=buf["N2"], r=buf["r"]))
+        run("gemm1", lambda: coda.coda_gemm(buf["N2"], T["W1"], buf["Y"]))
+        run("gemm_qkv", lambda: coda.coda_gemm(buf["N2"], T["W1r"], buf["Yr"]))
+        run("rope", lambda: coda.coda_unfused_rope(buf["Yr"], T["pos"], 500000.0, 64, n_rope))
+
+    return step
+
+
+def cold_cache(torch, coda, synth, p, T, dims, n_rope, total_flops, min_bytes=600 << 20, steps=30):
+    """Fused step with the inputs rotated over enough copies to exceed the MALL."""
+    M, d, K, N, NR = dims
+    keys = ("x", "W0", "z", "gamma", "W1", "W1r")
+    per_set = sum(T[k].numel() * T[k].element_size() for k in keys)
+    nsets = max(2, -(-min_bytes // per_set))
+    sets = []
+    for i in range(nsets):
+        Ti = dict(T)
+        for k in keys:
+            Ti[k] = T[k].clone()
+        sets.append(make_c2_step(torch, coda, Ti, dims, p["eps"])[0])
+    for st in sets:
+        st()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        sets[i % nsets]()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    del sets
+    return {"ms_per_step": round(ms, 5), "value": round(total_flops / (ms * 1e-3) / 1e12, 2), "input_sets": nsets,
+            "bytes_rotated": int(nsets * per_set), "steps": steps}
 
 
 def cpu_baseline(p, dims, n_rope, min_seconds=10.0, max_steps=20):
@@ -275,6 +336,154 @@ def bench_all(torch, coda, synth, iters=20):
     rec(5, "col_reduce", 0, d, 0, lambda: coda.coda_col_reduce(gpart, dg), aux_bytes=gpart.numel() * 4 + d * 4)
     dW = torch.empty(d, 2 * F, device="cuda")
     rec(5, "wgrad dWgu", d, 2 * F, M, lambda: coda.coda_gemm_wgrad(N2, dpre, dW))
+    del dOut, Wd, Wgu, pre, dpre, spart, s, u, gam, r, dU, N2, gpart, dg, dW
+    torch.cuda.empty_cache()
+    rows += bench_sequences(torch, coda, iters)
+    return rows
+
+
+def bench_sequences(torch, coda, iters=20):
+    """Each workload's fused call sequence against its unfused sequence (plain
+    GEMMs + standalone kernels) on the same tensors."""
+    bf = torch.bfloat16
+    rows = []
+
+    def rnd(*shape, std=1.0):
+        return (torch.randn(*shape, device="cuda") * std).to(bf)
+
+    def emp(*shape, dtype=bf):
+        return torch.empty(*shape, dtype=dtype, device="cuda")
+
+    def seq(cfg, name, flops, fused, unfused, it=iters):
+        fm, fmin = time_fn(torch, fused, it, 3)
+        um, umin = time_fn(torch, unfused, it, 3)
+        ent = {"config": cfg, "sequence": name, "gflop": round(flops / 1e9, 1),
+               "fused_us_median": round(fm * 1e3, 1), "fused_us_min": round(fmin * 1e3, 1),
+               "unfused_us_median": round(um * 1e3, 1), "unfused_us_min": round(umin * 1e3, 1),
+               "fused_tflops": round(flops / (fm * 1e-3) / 1e12, 1),
+               "unfused_tflops": round(flops / (um * 1e-3) / 1e12, 1),
+               "speedup": round(um / fm, 3)}
+        rows.append(ent)
+        log(json.dumps(ent))
+
+    # configs 1 and 2: GEMM -> residual -> RMSNorm -> GEMM (+ QKV GEMM with RoPE)
+    for cfg, (M, d, K, N, NR) in {1: (256, 512, 512, 1024, 0), 2: (8192, 2048, 2048, 2048, 3072)}.items():
+        x, W0, z, g = rnd(M, K), rnd(K, d, std=K ** -0.5), rnd(M, d), torch.ones(d, dtype=bf, device="cuda")
+        W1 = rnd(d, N, std=d ** -0.5)
+        U, H2, N2, Y0, Y = emp(M, d), emp(M, d), emp(M, d), emp(M, d), emp(M, N)
+        part, r = emp(M, coda.coda_nparts(d), dtype=torch.float32), emp(M, dtype=torch.float32)
+        if NR:
+            W1r, Yr = rnd(d, NR, std=d ** -0.5), emp(M, NR)
+            pos = torch.arange(M, device="cuda", dtype=torch.int32) % 2048
+
+        def fused():
+            coda.coda_gemm_res_sumsq(x, W0, z, g, U, H2, part)
+            coda.coda_row_rms(part, d, 1e-6, r)
+            coda.coda_gemm_rowscale(H2, W1, r, Y)
+            if NR:
+                coda.coda_gemm_rope(H2, W1r, r, pos, 5e5, 64, 2560, Yr)
+
+        def unfused():
+            coda.coda_gemm(x, W0, Y0)
+            coda.coda_unfused_add_rmsnorm(Y0, z, g, 1e-6, U, N2, r)
+            coda.coda_gemm(N2, W1, Y)
+            if NR:
+                coda.coda_gemm(N2, W1r, Yr)
+                coda.coda_unfused_rope(Yr, pos, 5e5, 64, 2560)
+
+        seq(cfg, "norm block forward", 2.0 * M * K * d + 2.0 * M * d * N + 2.0 * M * d * NR, fused, unfused)
+    # config 3: SwiGLU MLP forward and backward
+    M, d, F = 8192, 2048, 8192
+    x, Wgu, Wd, dY = rnd(M, d), rnd(d, 2 * F, std=d ** -0.5), rnd(F, d, std=F ** -0.5), rnd(M, d)
+    act, pre, out, o = emp(M, F), emp(M, 2 * F), emp(M, d), emp(M, d)
+
+    def f_fwd():
+        coda.coda_gemm_swiglu(x, Wgu, None, act, pre)
+        coda.coda_gemm_res_sumsq(act, Wd, x, U=out, want_part=False)
+
+    def u_fwd():
+        coda.coda_gemm(x, Wgu, pre)
+        coda.coda_unfused_swiglu(pre, act)
+        coda.coda_gemm(act, Wd, o)
+        coda.coda_unfused_add(o, x, out)
+
+    seq(3, "MLP forward", 2.0 * M * d * 2 * F + 2.0 * M * F * d, f_fwd, u_fwd)
+    da, dpre, dX, dX0 = emp(M, F), emp(M, 2 * F), emp(M, d), emp(M, d)
+    dWgu, dWd = emp(d, 2 * F, dtype=torch.float32), emp(F, d, dtype=torch.float32)
+
+    def f_bwd():
+        coda.coda_gemm_swiglu_bwd(dY, Wd, pre, dpre, want_spart=False)
+        coda.coda_gemm_res_sumsq_bwd(dpre, Wgu, X=x, dRes=dY, dX=dX, dW=dWgu)
+        coda.coda_gemm_wgrad(act, dY, dWd)
+
+    def u_bwd():
+        coda.coda_gemm_res_sumsq_bwd(dY, Wd, dX=da, want_dw=False)
+        coda.coda_unfused_swiglu_bwd(da, pre, dpre)
+        coda.coda_gemm_res_sumsq_bwd(dpre, Wgu, dX=dX0, want_dw=False)
+        coda.coda_unfused_add(dX0, dY, dX)
+        coda.coda_gemm_wgrad(x, dpre, dWgu)
+        coda.coda_gemm_wgrad(act, dY, dWd)
+
+    seq(3, "MLP backward", 2.0 * M * d * F + 2 * 2.0 * M * d * 2 * F + 2.0 * M * F * d, f_bwd, u_bwd, 10)
+    del x, Wgu, Wd, dY, act, pre, out, o, da, dpre, dX, dX0, dWgu, dWd
+    torch.cuda.empty_cache()
+    # config 4: LM head + cross-entropy, forward and backward
+    M, d, V = 8192, 2048, 128256
+    h, W = rnd(M, d), rnd(d, V, std=d ** -0.5)
+    labels = torch.randint(0, V, (M,), device="cuda", dtype=torch.int32)
+    ws = torch.empty(coda.coda_lmhead_ce_workspace(M, V), dtype=torch.uint8, device="cuda")
+    lse, lr, lm = emp(M, dtype=torch.float32), emp(M, dtype=torch.float32), emp(1, dtype=torch.float32)
+    L = emp(M, V)
+    seq(4, "LM head + CE forward", 2.0 * M * d * V, lambda: coda.coda_lmhead_ce(h, W, labels, lse, lr, lm, ws),
+        lambda: (coda.coda_gemm(h, W, L), coda.coda_unfused_cross_entropy(L, labels, lse, lr, lm)), 5)
+    dH, dW = emp(M, d), emp(d, V, dtype=torch.float32)
+    wsb = torch.empty(M * V * 2, dtype=torch.uint8, device="cuda")
+
+    def u_ce_bwd():
+        coda.coda_gemm(h, W, L)
+        coda.coda_unfused_cross_entropy(L, labels, lse, lr, lm)
+        coda.coda_unfused_cross_entropy_bwd(L, labels, lse, 1.0 / M, L)
+        coda.coda_gemm_res_sumsq_bwd(L, W, dX=dH, want_dw=False)
+        coda.coda_gemm_wgrad(h, L, dW)
+
+    def f_ce_bwd():
+        coda.coda_lmhead_ce(h, W, labels, lse, lr, lm, ws)
+        coda.coda_lmhead_ce_bwd(h, W, labels, lse, 1.0 / M, dH, dW, wsb)
+
+    # algorithmic work: the forward GEMM and the two gradient GEMMs (the fused
+    # backward's logit recomputation is not counted)
+    seq(4, "LM head + CE forward+backward", 3 * 2.0 * M * d * V, f_ce_bwd, u_ce_bwd, 3)
+    del h, W, ws, wsb, L, dH, dW
+    torch.cuda.empty_cache()
+    # config 5: one layer of the block backward (SwiGLU MLP + RMSNorm) at 8B-like shape
+    M, d, F = 8192, 4096, 14336
+    dOut, Wd, Wgu = rnd(M, d), rnd(F, d, std=F ** -0.5), rnd(d, 2 * F, std=d ** -0.5)
+    pre, act, u, N2 = rnd(M, 2 * F), rnd(M, F), rnd(M, d), rnd(M, d)
+    gam, r = torch.ones(d, dtype=bf, device="cuda"), torch.ones(M, device="cuda")
+    dpre, da, G, dU, N2f = emp(M, 2 * F), emp(M, F), emp(M, d), emp(M, d), emp(M, d)
+    spart, s_ = emp(M, coda.coda_nparts(F), dtype=torch.float32), emp(M, dtype=torch.float32)
+    gpart = emp(coda.coda_mparts(M), d, dtype=torch.float32)
+    gpu_ = emp(coda.coda_unfused_rmsnorm_bwd_parts(M), d, dtype=torch.float32)
+    dg, dWgu, dWd = emp(d, dtype=torch.float32), emp(d, 2 * F, dtype=torch.float32), emp(F, d, dtype=torch.float32)
+
+    def f_l():
+        coda.coda_gemm_swiglu_bwd(dOut, Wd, pre, dpre, spart)
+        coda.coda_row_rms_bwd(spart, d, s_)
+        coda.coda_gemm_rowscale_bwd(dpre, Wgu, u, gam, r, s_, dOut, dU, N2f, gpart)
+        coda.coda_col_reduce(gpart, dg)
+        coda.coda_gemm_wgrad(N2f, dpre, dWgu)
+        coda.coda_gemm_wgrad(act, dOut, dWd)
+
+    def u_l():
+        coda.coda_gemm_res_sumsq_bwd(dOut, Wd, dX=da, want_dw=False)
+        coda.coda_unfused_swiglu_bwd(da, pre, dpre)
+        coda.coda_gemm_res_sumsq_bwd(dpre, Wgu, dX=G, want_dw=False)
+        coda.coda_unfused_rmsnorm_bwd(G, u, gam, r, dOut, dU, gpu_)
+        coda.coda_col_reduce(gpu_, dg)
+        coda.coda_gemm_wgrad(N2, dpre, dWgu)
+        coda.coda_gemm_wgrad(act, dOut, dWd)
+
+    seq(5, "layer backward (SwiGLU MLP + RMSNorm)", 2.0 * M * d * F * 2 + 2 * 2.0 * M * d * 2 * F, f_l, u_l, 5)
     return rows
 
 
@@ -340,6 +549,28 @@ def main():
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
     op_ms = tm.mean_ms()
+    op_stats = tm.stats_ms()
+
+    # The unfused sequence of the same block, same inputs, same number of steps.
+    ustep = make_c2_unfused_step(torch, coda, T, dims, p["eps"], n_rope)
+    for _ in range(args.warmup):
+        ustep()
+    utm = OpTimer(torch)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        ustep(utm)
+    t_end.record()
+    torch.cuda.synchronize()
+    ums_step = t_start.elapsed_time(t_end) / args.steps
+    uops = {k: {"us_median": round(v[1] * 1e3, 2), "us_min": round(v[2] * 1e3, 2)}
+            for k, v in utm.stats_ms().items()}
+    log(f"unfused sequence: {ums_step * 1e3:.1f} us/step  {uops}")
+
+    # Cold cache: rotate input sets totalling more than 512 MB, so that no step
+    # finds its inputs in the 256 MB Infinity Cache.
+    cold = cold_cache(torch, coda, synth, p, T, dims, n_rope, total_flops)
+    log(f"cold cache: {cold}")
 
     value = total_flops / (ms_step * 1e-3) / 1e12
     dom = "rope"
@@ -347,7 +578,8 @@ def main():
     achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
     ops = {}
     for k, v in op_ms.items():
-        ent = {"us": round(v * 1e3, 2)}
+        ent = {"us": round(v * 1e3, 2), "us_median": round(op_stats[k][1] * 1e3, 2),
+               "us_min": round(op_stats[k][2] * 1e3, 2)}
         if k in flops:
             tf = flops[k] / (v * 1e-3) / 1e12
             ent.update(tflops=round(tf, 1), pct_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2))
@@ -389,6 +621,14 @@ def main():
             "calls": ["coda_gemm_res_sumsq", "coda_row_rms", "coda_gemm_rowscale", "coda_gemm_rope"],
         },
         "ops": ops,
+        "unfused": {
+            "ms_per_step": round(ums_step, 5),
+            "value": round(total_flops / (ums_step * 1e-3) / 1e12, 2),
+            "fused_speedup": round(ums_step / ms_step, 4),
+            "calls": ["coda_gemm", "coda_unfused_add_rmsnorm", "coda_gemm", "coda_gemm", "coda_unfused_rope"],
+            "ops": uops,
+        },
+        "cold_cache": cold,
         "roofline": {
             "bound": "mfma",
             "kernel": "coda_gemm_rope (8192x3072x2048)",

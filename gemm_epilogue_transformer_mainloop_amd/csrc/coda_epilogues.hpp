@@ -358,34 +358,60 @@ struct EpiCE {
     for (int ci = 0; ci < CI; ++ci) {
       const int t = g.tw0 + L.t(ci);
       const bool tok_ok = L.tok(ci);
-      // feature index of the label relative to this lane's first feature
-      const int label = tok_ok ? vload(labels, t, g.T) - g.fw0 : -1;
+      // Label position relative to the wave tile: 8-feature group grp (held by
+      // this lane when grp == 4 ri + 2 h + hh) and element eo inside it.
+      const int rel = tok_ok ? vload(labels, t, g.T) - g.fw0 : -1;
+      const int grp = rel >> 3, eo = rel & 7;
+      const bool b0 = (eo & 1) != 0, b1 = (eo & 2) != 0, b2 = (eo & 4) != 0;
       float l[RI][2][8];
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
         for (int h = 0; h < 2; ++h) acc8(acc, ri, ci, h, l[ri][h]);
+      // Max and sum-exp per 8-feature group; a group lies entirely inside or
+      // entirely past the vocabulary (V % 8 == 0), so masking is per group.
       float m = -INFINITY;
+      bool gv[RI][2];
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h) {
+          float gm = l[ri][h][0];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) m = (L.f(ri, h) + e < L.F) ? fmaxf(m, l[ri][h][e]) : m;
-      float s = 0.0f, tv = 0.0f;
+          for (int e = 1; e < 8; ++e) gm = fmaxf(gm, l[ri][h][e]);
+          gv[ri][h] = L.f(ri, h) < L.F;
+          m = gv[ri][h] ? fmaxf(m, gm) : m;
+        }
+      const float ml = m * LOG2E;
+      float s = 0.0f;
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float gs = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gs += __builtin_amdgcn_exp2f(fmaf(l[ri][h][e], LOG2E, -ml));
+          s += gv[ri][h] ? gs : 0.0f;
+        }
+      // Target gather: the group that holds the label (one compare per
+      // group), then its element eo by a 3-level select.
+      float gsel[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gsel[e] = 0.0f;
       bool hit = false;
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h) {
+          const bool hg = grp == ri * 4 + h * 2 + g.hh;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int fe = L.f(ri, h) + e;
-            s += (fe < L.F) ? fast_exp(l[ri][h][e] - m) : 0.0f;
-            const bool is = label == fe;
-            tv = is ? l[ri][h][e] : tv;
-            hit = hit || is;
-          }
+          for (int e = 0; e < 8; ++e) gsel[e] = hg ? l[ri][h][e] : gsel[e];
+          hit = hit || hg;
+        }
+      const float s01 = b0 ? gsel[1] : gsel[0], s23 = b0 ? gsel[3] : gsel[2];
+      const float s45 = b0 ? gsel[5] : gsel[4], s67 = b0 ? gsel[7] : gsel[6];
+      const float s03 = b1 ? s23 : s01, s47 = b1 ? s67 : s45;
+      const float tv = b2 ? s47 : s03;
       if (hit) tgt[t] = tv;
       // merge the two half-wave states of this token
       const float m2 = __shfl_xor(m, 32), s2 = __shfl_xor(s, 32);
@@ -656,13 +682,13 @@ struct EpiF32 {
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h) {
+          float a[8];
+          if constexpr (ACCUM) acc8(acc, ri, ci, h, a);
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             f32x4 v;
             if constexpr (ACCUM) {
-              float a[8];
-              acc8(acc, ri, ci, h, a);
               v = (f32x4){a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]} +
                   __builtin_bit_cast(f32x4, prev[ci & 1][ri][h][c]);
             } else {  // stored straight from the accumulator registers
@@ -671,6 +697,7 @@ struct EpiF32 {
             }
             o.store16(L.t(ci), L.f(ri, h) + 4 * c, L.ok(ci, ri, h), __builtin_bit_cast(u32x4, v));
           }
+        }
     }
   }
 };
