@@ -62,10 +62,14 @@ def parse_resources(text: str) -> dict:
     return out
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, occ2: bool = False, out: str = None) -> str:
+    """Build the library.  occ2=True builds the variant whose forward and
+    data-gradient calls use two workgroups per CU (coda_mainloop_occ2.hpp)
+    into `out` (default libcoda_occ2.so); the default library does not use it."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + srcs + ["-o", tmp]
+    lib = out or (os.path.join(HERE, "libcoda_occ2.so") if occ2 else LIB)
+    tmp = lib + ".tmp"
+    cmd = [HIPCC] + FLAGS + (["-DCODA_OCC2=1"] if occ2 else []) + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -82,11 +86,12 @@ def build(verbose: bool = False) -> str:
     if spills:
         os.remove(tmp)
         raise RuntimeError(f"kernels use scratch memory (register spills): {spills}")
-    with open(RESOURCES, "w") as f:
-        json.dump(resources, f, indent=1, sort_keys=True)
-    os.replace(tmp, LIB)
-    return LIB
+    if not occ2:
+        with open(RESOURCES, "w") as f:
+            json.dump(resources, f, indent=1, sort_keys=True)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, occ2="--occ2" in sys.argv[1:]))

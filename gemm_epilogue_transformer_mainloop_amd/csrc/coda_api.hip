@@ -9,10 +9,12 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "../../include/coda.h"
 #include "coda_epilogues.hpp"
 #include "coda_host.hpp"
+#include "coda_mainloop_occ2.hpp"
 
 using namespace coda;
 using namespace coda_host;
@@ -90,9 +92,43 @@ __global__ void __launch_bounds__(1024) mean_kernel(const float* __restrict__ x,
 }
 
 // Launch one fused GEMM: features F (output columns), tokens T (output rows).
+// Epilogues that work on any wave-tile width (all but the dgamma column
+// partials, which are laid out per 128-token wave tile).
+template <class Epi>
+struct AnyWaveWidth : std::true_type {};
+template <bool A, bool B, bool C>
+struct AnyWaveWidth<EpiRowscaleBwd<A, B, C>> : std::false_type {};
+
+#ifndef CODA_OCC2
+#define CODA_OCC2 0
+#endif
+
+// Two workgroups per CU (256 x 128 tiles, coda_mainloop_occ2.hpp).
+template <bool WK, class Epi>
+coda_status launch_gemm_occ2(const uint16_t* W, int ldw, const uint16_t* X, int ldx, int F, int T, int K,
+                             const Epi& epi, hipStream_t stream) {
+  Problem p;
+  p.W = W;
+  p.X = X;
+  p.ldw = ldw;
+  p.ldx = ldx;
+  p.F = F;
+  p.T = T;
+  p.K = K;
+  p.nTF = cdiv(F, occ2::BF);
+  p.nTT = cdiv(T, occ2::BT);
+  const int nb = p.nTF * p.nTT;
+  if (nb == 0) return CODA_OK;
+  hipLaunchKernelGGL((occ2::gemm_epi_kernel_occ2<WK, Epi>), dim3(nb), dim3(NT), 0, stream, p, epi);
+  return launched();
+}
+
 template <bool WK, bool XK, int BT = 256, class Epi>
 coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, int F, int T, int K,
                         const Epi& epi, hipStream_t stream) {
+  if constexpr (CODA_OCC2 && XK && AnyWaveWidth<Epi>::value) {
+    return launch_gemm_occ2<WK>(W, ldw, X, ldx, F, T, K, epi, stream);
+  }
   constexpr int BF = 256;
   Problem p;
   p.W = W;

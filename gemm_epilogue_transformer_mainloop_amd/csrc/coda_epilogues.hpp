@@ -483,7 +483,10 @@ struct EpiSwigluBwd {
     // The feature space of this GEMM is F (da_j); pre/dpre columns are 2j, 2j+1.
     const TileView<2> pi(pre, ldp, g.tw0, 2 * g.fw0);
     const TileView<2> po(dpre, lddp, g.tw0, 2 * g.fw0);
-    u32x4 pv[2][RI][2][2];
+    // Double-buffered per 32-token column when the wave has 4 columns; with 2
+    // (two workgroups per CU) one buffer keeps the wave within 128 VGPRs.
+    constexpr int NB = CI > 2 ? 2 : 1;
+    u32x4 pv[NB][RI][2][2];
     auto load_col = [&](int ci, u32x4 (&b)[RI][2][2]) {
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
@@ -492,10 +495,14 @@ struct EpiSwigluBwd {
 #pragma unroll
           for (int c = 0; c < 2; ++c) b[ri][h][c] = pi.load16(L.t(ci), 2 * L.f(ri, h) + 8 * c, L.ok(ci, ri, h));
     };
-    load_col(0, pv[0]);
+    if constexpr (NB == 2) load_col(0, pv[0]);
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
-      if (ci + 1 < CI) load_col(ci + 1, pv[(ci + 1) & 1]);
+      if constexpr (NB == 2) {
+        if (ci + 1 < CI) load_col(ci + 1, pv[(ci + 1) & 1]);
+      } else {
+        load_col(ci, pv[0]);
+      }
       float ss = 0.0f;
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
@@ -507,7 +514,7 @@ struct EpiSwigluBwd {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {  // two 16-byte chunks = 4 pairs each
             float pvv[8], out[8];
-            unpack8(pv[ci & 1][ri][h][c], pvv);
+            unpack8(pv[ci % NB][ri][h][c], pvv);
             float part = 0.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {

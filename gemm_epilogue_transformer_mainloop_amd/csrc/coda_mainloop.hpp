@@ -109,9 +109,11 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t range, uint32_t
   rs[2] = __builtin_amdgcn_readfirstlane((int)range);
   rs[3] = 0x00020000;
   const int m0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_ptr_t)dst);
+  // A SALU write of M0 needs one wait state before an LDS-DMA instruction
+  // reads it; s_nop 1 gives two.
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
-      "s_nop 4\n\t"
+      "s_nop 1\n\t"
       "buffer_load_dwordx4 %0, %1, 0 offen lds"
       :
       : "v"(voff), "s"(rs), "s"(m0)
