@@ -58,18 +58,18 @@ __global__ void col_reduce_kernel(const float* __restrict__ gpart, int mparts, i
 }
 
 // Merge of per-tile (max, sum exp) into lse and the row loss (notes sec. 2).
+// Partials are part-major ([nparts x M]): consecutive threads read
+// consecutive tokens.
 __global__ void ce_reduce_kernel(const float* __restrict__ pm, const float* __restrict__ ps,
                                  const float* __restrict__ tgt, const int32_t* __restrict__ labels,
                                  int nparts, int M, int V, float* __restrict__ lse,
                                  float* __restrict__ loss) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= M) return;
-  const float* m = pm + (size_t)i * nparts;
-  const float* s = ps + (size_t)i * nparts;
   float L = -INFINITY;
-  for (int j = 0; j < nparts; ++j) L = fmaxf(L, m[j]);
+  for (int j = 0; j < nparts; ++j) L = fmaxf(L, pm[(size_t)j * M + i]);
   float S = 0.0f;
-  for (int j = 0; j < nparts; ++j) S += s[j] * expf(m[j] - L);
+  for (int j = 0; j < nparts; ++j) S += ps[(size_t)j * M + i] * expf(pm[(size_t)j * M + i] - L);
   const float l = L + logf(S);
   lse[i] = l;
   const int y = labels[i];
@@ -367,7 +367,7 @@ coda_status coda_lmhead_ce(const coda_bf16* H, int ldh, const coda_bf16* W, int 
   float* tgt = ps + (size_t)M * np;
   float* lrow = tgt + M;
   if (loss_row == nullptr) loss_row = lrow;
-  EpiCE e{labels, pm, ps, tgt, np};
+  EpiCE e{labels, pm, ps, tgt, M};
   if (coda_status s = launch_gemm<false, true>(W, ldw, H, ldh, V, M, d, e, stream)) return s;
   hipLaunchKernelGGL(ce_reduce_kernel, dim3(cdiv(M, 256)), dim3(256), 0, stream, pm, ps, tgt,
                      labels, np, M, V, lse, loss_row);

@@ -346,10 +346,10 @@ struct EpiSwiglu {
 // ---------------------------------------------------------------------------
 struct EpiCE {
   const int32_t* labels;
-  float* part_m;
+  float* part_m;  // [nparts x ldpart], ldpart >= M
   float* part_s;
   float* tgt;
-  int nparts;
+  int ldpart;
 
   template <int RI, int CI>
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
@@ -419,8 +419,9 @@ struct EpiCE {
       const float st = (m == -INFINITY ? 0.0f : s * fast_exp(m - mm)) +
                        (m2 == -INFINITY ? 0.0f : s2 * fast_exp(m2 - mm));
       if (g.hh == 0 && tok_ok && L.F > 0) {
-        part_m[(size_t)t * nparts + g.pf] = mm;
-        part_s[(size_t)t * nparts + g.pf] = st;
+        // part-major [nparts x M]: the 32 lanes write 128 contiguous bytes
+        part_m[(size_t)g.pf * ldpart + t] = mm;
+        part_s[(size_t)g.pf * ldpart + t] = st;
       }
     }
   }
