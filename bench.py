@@ -86,18 +86,19 @@ class OpTimer:
 
 
 def time_fn(torch, fn, iters=20, warmup=5):
+    """Median and min over `iters` back-to-back calls, each bracketed by HIP
+    events on the current stream (one synchronisation at the end, so the
+    host never makes the GPU wait between calls)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    times = []
-    for _ in range(iters):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for s, e in ev:
         s.record()
         fn()
         e.record()
-        e.synchronize()
-        times.append(s.elapsed_time(e))
+    torch.cuda.synchronize()
+    times = [s.elapsed_time(e) for s, e in ev]
     return float(np.median(times)), float(np.min(times))
 
 
@@ -484,6 +485,87 @@ def bench_sequences(torch, coda, iters=20):
         coda.coda_gemm_wgrad(act, dOut, dWd)
 
     seq(5, "layer backward (SwiGLU MLP + RMSNorm)", 2.0 * M * d * F * 2 + 2 * 2.0 * M * d * 2 * F, f_l, u_l, 5)
+    del dOut, Wd, Wgu, pre, act, u, N2, gam, r, dpre, da, G, dU, N2f, spart, s_, gpart, gpu_, dg, dWgu, dWd
+    torch.cuda.empty_cache()
+    rows += bench_block(torch, coda, seq_fn=seq)
+    return rows
+
+
+def bench_block(torch, coda, seq_fn):
+    """The whole config-5 block (W0 projection + two residual/RMSNorm/SwiGLU-MLP
+    layers), forward and backward as one stream ("CODA" paper Figure 11):
+    the fused calls against the unfused sequence."""
+    bf, f32 = torch.bfloat16, torch.float32
+    M, d, F, eps = 8192, 4096, 14336, 1e-6
+
+    def rnd(*shape, std=1.0):
+        return (torch.randn(*shape, device="cuda") * std).to(bf)
+
+    def emp(*shape, dtype=bf):
+        return torch.empty(*shape, dtype=dtype, device="cuda")
+
+    x, z, dOut, W0 = rnd(M, d), rnd(M, d), rnd(M, d), rnd(d, d, std=d ** -0.5)
+    L = [dict(g=(1.0 + 0.1 * torch.randn(d, device="cuda")).to(bf), Wgu=rnd(d, 2 * F, std=d ** -0.5),
+              Wd=rnd(F, d, std=F ** -0.5)) for _ in range(2)]
+    # activations (shared shapes by both paths) and gradients
+    A = [dict(u=emp(M, d), h=emp(M, d), part=emp(M, coda.coda_nparts(d), dtype=f32), r=emp(M, dtype=f32),
+              pre=emp(M, 2 * F), a=emp(M, F), dpre=emp(M, 2 * F), du=emp(M, d), n2=emp(M, d),
+              sp=emp(M, coda.coda_nparts(F), dtype=f32), s=emp(M, dtype=f32),
+              gp=emp(coda.coda_mparts(M), d, dtype=f32), gpu=emp(coda.coda_unfused_rmsnorm_bwd_parts(M), d, dtype=f32),
+              dg=emp(d, dtype=f32), dWgu=emp(d, 2 * F, dtype=f32), dWd=emp(F, d, dtype=f32), da=emp(M, F),
+              G=emp(M, d), y=emp(M, d)) for _ in range(2)]
+    out, dx, dW0, Y0, T = emp(M, d), emp(M, d), emp(d, d, dtype=f32), emp(M, d), emp(M, d)
+
+    def fused():
+        a1, a2 = A
+        coda.coda_gemm_res_sumsq(x, W0, z, L[0]["g"], a1["u"], a1["h"], a1["part"])
+        coda.coda_row_rms(a1["part"], d, eps, a1["r"])
+        coda.coda_gemm_swiglu(a1["h"], L[0]["Wgu"], a1["r"], a1["a"], a1["pre"])
+        coda.coda_gemm_res_sumsq(a1["a"], L[0]["Wd"], a1["u"], L[1]["g"], a2["u"], a2["h"], a2["part"])
+        coda.coda_row_rms(a2["part"], d, eps, a2["r"])
+        coda.coda_gemm_swiglu(a2["h"], L[1]["Wgu"], a2["r"], a2["a"], a2["pre"])
+        coda.coda_gemm_res_sumsq(a2["a"], L[1]["Wd"], a2["u"], U=out, want_part=False)
+        dres = dOut
+        for l in (1, 0):
+            c, W = A[l], L[l]
+            coda.coda_gemm_wgrad(c["a"], dres, c["dWd"])
+            coda.coda_gemm_swiglu_bwd(dres, W["Wd"], c["pre"], c["dpre"], c["sp"])
+            coda.coda_row_rms_bwd(c["sp"], d, c["s"])
+            coda.coda_gemm_rowscale_bwd(c["dpre"], W["Wgu"], c["u"], W["g"], c["r"], c["s"], dres, c["du"], c["n2"],
+                                        c["gp"])
+            coda.coda_col_reduce(c["gp"], c["dg"])
+            coda.coda_gemm_wgrad(c["n2"], c["dpre"], c["dWgu"])
+            dres = c["du"]
+        coda.coda_gemm_res_sumsq_bwd(A[0]["du"], W0, X=x, dX=dx, dW=dW0)
+
+    def unfused():
+        a1, a2 = A
+        coda.coda_gemm(x, W0, Y0)
+        coda.coda_unfused_add_rmsnorm(Y0, z, L[0]["g"], eps, a1["u"], a1["n2"], a1["r"])
+        coda.coda_gemm(a1["n2"], L[0]["Wgu"], a1["pre"])
+        coda.coda_unfused_swiglu(a1["pre"], a1["a"])
+        coda.coda_gemm(a1["a"], L[0]["Wd"], T)
+        coda.coda_unfused_add_rmsnorm(T, a1["u"], L[1]["g"], eps, a2["u"], a2["n2"], a2["r"])
+        coda.coda_gemm(a2["n2"], L[1]["Wgu"], a2["pre"])
+        coda.coda_unfused_swiglu(a2["pre"], a2["a"])
+        coda.coda_gemm(a2["a"], L[1]["Wd"], T)
+        coda.coda_unfused_add(T, a2["u"], out)
+        dres = dOut
+        for l in (1, 0):
+            c, W = A[l], L[l]
+            coda.coda_gemm_wgrad(c["a"], dres, c["dWd"])
+            coda.coda_gemm_res_sumsq_bwd(dres, W["Wd"], dX=c["da"], want_dw=False)
+            coda.coda_unfused_swiglu_bwd(c["da"], c["pre"], c["dpre"])
+            coda.coda_gemm_res_sumsq_bwd(c["dpre"], W["Wgu"], dX=c["G"], want_dw=False)
+            coda.coda_unfused_rmsnorm_bwd(c["G"], c["u"], W["g"], c["r"], dres, c["du"], c["gpu"])
+            coda.coda_col_reduce(c["gpu"], c["dg"])
+            coda.coda_gemm_wgrad(c["n2"], c["dpre"], c["dWgu"])
+            dres = c["du"]
+        coda.coda_gemm_res_sumsq_bwd(A[0]["du"], W0, X=x, dX=dx, dW=dW0)
+
+    fwd = 2.0 * M * d * d + 2 * (2.0 * M * d * 2 * F + 2.0 * M * F * d)
+    rows = []
+    seq_fn(5, "block forward+backward (W0 + 2 layers)", 3 * fwd, fused, unfused, 3)
     return rows
 
 
