@@ -34,6 +34,7 @@ _SIGS = {
     "coda_version": (ctypes.c_char_p, []),
     "coda_nparts": (I, [I]),
     "coda_mparts": (I, [I]),
+    "coda_tile_split": (I, [I, I, I]),
     "coda_lmhead_ce_workspace": (SZ, [I, I]),
     "coda_lmhead_ce_bwd_workspace": (SZ, [I, I, I]),
     "coda_gemm": (I, [P, I, P, I, P, I, I, I, I, P]),
@@ -151,6 +152,10 @@ def coda_nparts(N: int) -> int:
 
 def coda_mparts(M: int) -> int:
     return int(lib().coda_mparts(M))
+
+
+def coda_tile_split(F: int, T: int, cus: int) -> int:
+    return int(lib().coda_tile_split(F, T, cus))
 
 
 def coda_lmhead_ce_workspace(M: int, V: int) -> int:

@@ -117,10 +117,34 @@ coda_status launch_gemm_occ2(const uint16_t* W, int ldw, const uint16_t* X, int 
   p.K = K;
   p.nTF = cdiv(F, occ2::BF);
   p.nTT = cdiv(T, occ2::BT);
+  p.f_base = 0;
   const int nb = p.nTF * p.nTT;
   if (nb == 0) return CODA_OK;
   hipLaunchKernelGGL((occ2::gemm_epi_kernel_occ2<WK, Epi>), dim3(nb), dim3(NT), 0, stream, p, epi);
   return launched();
+}
+
+// Tile-count quantization.  One 256x256 tile per CU at a time: when the tile
+// count leaves the last round of tiles partly empty (8192 x 3072 has 384
+// tiles = 1.5 rounds on 256 CUs), the trailing feature range can instead be
+// covered by 256-feature x 128-token tiles, which take about half as long and
+// come two per big tile.  Returns the number of 256-wide feature tiles to
+// keep in big tiles (the rest go to the half tiles), or 0 to keep every tile
+// big.  Cost model in rounds: a big round is 1, a half-tile round 0.55; a
+// split must save at least 0.2 rounds.
+inline int quantization_split(int nTF, int nTT, int nTT_half, int cus) {
+  if (cus <= 0 || nTF < 2) return 0;
+  const double base = (double)cdiv(nTF * nTT, cus);
+  double best = base - 0.2;
+  int split = 0;
+  for (int f1 = 1; f1 < nTF; ++f1) {
+    const double c = (double)cdiv(f1 * nTT, cus) + 0.55 * (double)cdiv((nTF - f1) * nTT_half, cus);
+    if (c < best) {
+      best = c;
+      split = f1;
+    }
+  }
+  return split;
 }
 
 template <bool WK, bool XK, int BT = 256, class Epi>
@@ -140,8 +164,25 @@ coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, 
   p.K = K;
   p.nTF = cdiv(F, BF);
   p.nTT = cdiv(T, BT);
+  p.f_base = 0;
   const int nb = p.nTF * p.nTT;
   if (nb == 0) return CODA_OK;
+  if constexpr (BT == 256 && XK && AnyWaveWidth<Epi>::value) {
+    const int split = coda_tile_split(F, T, device_cus());
+    if (split > 0) {
+      Problem big = p, half = p;
+      big.nTF = split;
+      half.f_base = split * BF;
+      half.nTF = p.nTF - split;
+      half.nTT = cdiv(T, 128);
+      hipLaunchKernelGGL((gemm_epi_kernel<BF, BT, WK, XK, Epi>), dim3(big.nTF * big.nTT), dim3(NT), 0, stream,
+                         big, epi);
+      if (hipPeekAtLastError() != hipSuccess) return launched();
+      hipLaunchKernelGGL((gemm_epi_kernel<BF, 128, WK, XK, Epi>), dim3(half.nTF * half.nTT), dim3(NT), 0,
+                         stream, half, epi);
+      return launched();
+    }
+  }
   hipLaunchKernelGGL((gemm_epi_kernel<BF, BT, WK, XK, Epi>), dim3(nb), dim3(NT), 0, stream, p, epi);
   return launched();
 }
@@ -171,6 +212,10 @@ const char* coda_version(void) { return "coda-gfx950 0.1"; }
 
 int coda_nparts(int N) { return N <= 0 ? 0 : cdiv(N, WAVE_F); }
 int coda_mparts(int M) { return M <= 0 ? 0 : cdiv(M, WAVE_T); }
+int coda_tile_split(int F, int T, int cus) {
+  if (F <= 0 || T <= 0) return 0;
+  return quantization_split(cdiv(F, 256), cdiv(T, 256), cdiv(T, 128), cus);
+}
 
 size_t coda_lmhead_ce_workspace(int M, int V) {
   if (M <= 0 || V <= 0) return 0;

@@ -76,6 +76,20 @@ inline coda_status device_ok() {
   return v == 1 ? CODA_OK : CODA_ERR_UNSUPPORTED;
 }
 
+// Compute units of the current device, cached per device (0 if unknown).
+inline std::atomic<int> g_cus[64];
+
+inline int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = g_cus[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 0;
+    g_cus[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 inline coda_status launched() { return hipGetLastError() == hipSuccess ? CODA_OK : CODA_ERR_HIP; }
 
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }

@@ -221,6 +221,7 @@ struct Problem {
   int ldw, ldx;
   int F, T, K;        // output features, tokens, reduction length
   int nTF, nTT;       // tile counts along F and T
+  int f_base;         // first feature of this launch (tiles cover [f_base, F))
 };
 
 // What one lane needs to place its accumulators.
@@ -283,7 +284,7 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
   const int lt = lane & 31, hh = lane >> 5;
   int tf, tt;
   tile_coords(blockIdx.x, gridDim.x, p.nTF, p.nTT, tf, tt);
-  const int f0 = tf * BF, t0 = tt * BT;
+  const int f0 = p.f_base + tf * BF, t0 = tt * BT;
 
   f32x16 acc[RI][CI];
 #pragma unroll

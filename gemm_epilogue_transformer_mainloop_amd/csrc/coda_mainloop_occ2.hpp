@@ -111,7 +111,7 @@ __global__ void __launch_bounds__(NT, 2) gemm_epi_kernel_occ2(const Problem p, c
   const int lt = lane & 31, hh = lane >> 5;
   int tf, tt;
   tile_coords(blockIdx.x, gridDim.x, p.nTF, p.nTT, tf, tt);
-  const int f0 = tf * BF, t0 = tt * BT;
+  const int f0 = p.f_base + tf * BF, t0 = tt * BT;
 
   f32x16 acc[RI][CI];
 #pragma unroll

@@ -66,6 +66,17 @@ int coda_nparts(int N);
  * tokens (one per 128-token wavefront output tile): ceil(M / 128). */
 int coda_mparts(int M);
 
+/* Tile plan of a fused GEMM with F output features (N, F or V of the call)
+ * and T tokens (M) on a device with `cus` compute units.  Output tiles are
+ * 256 features x 256 tokens, one per compute unit at a time; when that
+ * leaves the last round of tiles mostly empty, the features from
+ * 256 * split on are computed in 256 x 128 tiles in a second launch.
+ * Returns split (0: all tiles 256 x 256).  Applies to coda_gemm, the forward
+ * calls, coda_gemm_swiglu_bwd, coda_gemm_res_sumsq_bwd (dX) and the GEMMs
+ * of the LM head; coda_gemm_rowscale_bwd and the weight gradients always use
+ * 256 x 256 tiles.  Host-only: touches no device. */
+int coda_tile_split(int F, int T, int cus);
+
 /* Workspace bytes coda_lmhead_ce needs for M rows and vocabulary V. */
 size_t coda_lmhead_ce_workspace(int M, int V);
 
@@ -117,7 +128,8 @@ coda_status coda_gemm_rowscale(const coda_bf16* A, int lda, const coda_bf16* W, 
  *   ang = pos_i * theta^(-2k / head_dim):
  *     (y_c, y_c+1) = (t_c cos - t_c+1 sin, t_c sin + t_c+1 cos)
  *   columns >= n_rope pass through.  pos is int32 [M].
- * Needs head_dim even, n_rope % head_dim == 0 and n_rope <= N. */
+ * Needs head_dim even, n_rope % head_dim == 0, n_rope % 8 == 0 and
+ * n_rope <= N. */
 coda_status coda_gemm_rope(const coda_bf16* A, int lda, const coda_bf16* W, int ldw,
                            const float* r, const int32_t* pos, float theta, int head_dim,
                            int n_rope, coda_bf16* Y, int ldy, int M, int N, int K,

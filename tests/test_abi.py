@@ -50,6 +50,39 @@ def test_queries(L):
     assert coda.coda_lmhead_ce_bwd_workspace(100, V, 2048) == 100 * V * 2
 
 
+def test_tile_split(L):
+    """Tile-count quantization plan (host logic; 256 compute units)."""
+    cus = 256
+    # QKV 8192 x 3072: 384 big tiles = 1.5 rounds -> 8 feature tiles big, 4 in half tiles
+    assert coda.coda_tile_split(3072, 8192, cus) == 8
+    # whole rounds stay big: 2048, 16384, 8192 and 14336 features at 8192 tokens
+    for F in (2048, 4096, 8192, 14336, 16384, 28672):
+        assert coda.coda_tile_split(F, 8192, cus) == 0, F
+    # LM head: 16032 tiles, the partial last round costs < 1%, no split
+    assert coda.coda_tile_split(128256, 8192, cus) == 0
+    # one tile, or a single feature tile: nothing to split
+    assert coda.coda_tile_split(256, 256, cus) == 0
+    assert coda.coda_tile_split(200, 1 << 20, cus) == 0
+    # 3 x 96 = 288 tiles (2 rounds) -> 2 big feature tiles (1 round) + 192 half tiles
+    assert coda.coda_tile_split(712, 24500, cus) == 2
+    # 4 x 96 = 384 tiles: the half tiles would need 2 rounds, no gain worth it
+    assert coda.coda_tile_split(776, 24500, cus) == 0
+    # unknown CU count or empty problems
+    assert coda.coda_tile_split(3072, 8192, 0) == 0
+    assert coda.coda_tile_split(0, 8192, cus) == 0
+    assert coda.coda_tile_split(3072, 0, cus) == 0
+    # other CU counts: the plan always lowers the modelled round count
+    for cus2 in (32, 80, 304):
+        for F in (768, 3072, 5120):
+            s = coda.coda_tile_split(F, 8192, cus2)
+            nF, nT = -(-F // 256), 32
+            base = -(-nF * nT // cus2)
+            if s:
+                assert 0 < s < nF
+                cost = -(-s * nT // cus2) + 0.55 * -(-(nF - s) * 64 // cus2)
+                assert cost <= base - 0.2
+
+
 # Fake, 256-byte aligned, never dereferenced: every call below fails validation first.
 A16 = ctypes.c_void_p(0x100000)
 A16b = ctypes.c_void_p(0x200000)
@@ -144,5 +177,9 @@ def test_no_kernel_spills():
     assert len(gemm) >= 20
     for name, v in res.items():
         assert v["scratch"] == 0 and v["vgpr_spill"] == 0, name
-    # the main loop holds the 128x128 wave tile in the 256 accumulation registers
-    assert all(v["agprs"] == 256 for v in gemm.values())
+    # the main loop holds the 128x128 wave tile in the 256 accumulation
+    # registers; the 256x128-tile kernels (tile-count split) hold 128x64
+    half = {k: v for k, v in gemm.items() if "ILi256ELi128E" in k}
+    assert half, "no 256x128-tile kernels"
+    assert all(v["agprs"] == 256 for k, v in gemm.items() if k not in half)
+    assert all(v["agprs"] == 128 for v in half.values())
