@@ -104,6 +104,9 @@ struct EpiLinear {
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
     const Lane L(g);
     const TileView<2> y(Y, ldy, g.tw0, g.fw0);
+    float rsv[CI];
+#pragma unroll
+    for (int ci = 0; ci < CI; ++ci) rsv[ci] = HAS_R ? vload(r, g.tw0 + L.t(ci), g.T) : 1.0f;
     u32x4 rv[CI][RI][2];
     if constexpr (HAS_RES) {
       const TileView<2> rz(res, ldres, g.tw0, g.fw0);
@@ -116,7 +119,7 @@ struct EpiLinear {
     }
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
-      const float rs = HAS_R ? vload(r, g.tw0 + L.t(ci), g.T) : 1.0f;
+      const float rs = rsv[ci];
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
@@ -238,27 +241,39 @@ struct EpiRope {
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
     const Lane L(g);
     const TileView<2> y(Y, ldy, g.tw0, g.fw0);
+    float rsv[CI], psv[CI];
+#pragma unroll
+    for (int ci = 0; ci < CI; ++ci) {
+      const int t = g.tw0 + L.t(ci);
+      rsv[ci] = HAS_R ? vload(r, t, g.T) : 1.0f;
+      psv[ci] = (float)vload(pos, t, g.T);
+    }
     // Per-lane frequencies in revolutions per position: theta^(-2k/hd) / (2 pi);
     // 0 for pass-through columns (angle 0 rotates by the identity).
+    // The pair at column c = f + 2q (f a multiple of 8) has 2k = c mod head_dim:
+    // one modulo per 8-column run, then at most three wraps (head_dim >= 2).
     constexpr float INV_2PI = 0.15915494309189535f;
+    const float c_exp = log2_theta / (float)head_dim;
     float fr[RI][2][4];
 #pragma unroll
     for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int f = g.fw0 + L.f(ri, h);
+        const int base = f % head_dim;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int k = ((f + 2 * q) % head_dim) >> 1;
-          const float w = exp2f(-(float)(2 * k) / (float)head_dim * log2_theta) * INV_2PI;
+          int j = base + 2 * q;
+          j -= j >= head_dim ? head_dim : 0;
+          j -= j >= head_dim ? head_dim : 0;
+          j -= j >= head_dim ? head_dim : 0;
+          const float w = exp2f(-(float)j * c_exp) * INV_2PI;
           fr[ri][h][q] = f < n_rope ? w : 0.0f;
         }
       }
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
-      const int t = g.tw0 + L.t(ci);
-      const float rs = HAS_R ? vload(r, t, g.T) : 1.0f;
-      const float ps = (float)vload(pos, t, g.T);
+      const float rs = rsv[ci], ps = psv[ci];
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
@@ -299,9 +314,12 @@ struct EpiSwiglu {
     const Lane L(g);
     const TileView<2> ao(act, ldact, g.tw0, g.fw0 >> 1);
     const TileView<2> po(pre, ldp, g.tw0, g.fw0);
+    float rsv[CI];
+#pragma unroll
+    for (int ci = 0; ci < CI; ++ci) rsv[ci] = HAS_R ? vload(r, g.tw0 + L.t(ci), g.T) : 1.0f;
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
-      const float rs = HAS_R ? vload(r, g.tw0 + L.t(ci), g.T) : 1.0f;
+      const float rs = rsv[ci];
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri) {
         // a-columns of this lane: 16 ri + 8 h + 4 hh + q (q = 0..3) for half h
@@ -354,13 +372,16 @@ struct EpiCE {
   template <int RI, int CI>
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
     const Lane L(g);
+    int lab[CI];
+#pragma unroll
+    for (int ci = 0; ci < CI; ++ci) lab[ci] = vload(labels, g.tw0 + L.t(ci), g.T);
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
       const int t = g.tw0 + L.t(ci);
       const bool tok_ok = L.tok(ci);
       // Label position relative to the wave tile: 8-feature group grp (held by
       // this lane when grp == 4 ri + 2 h + hh) and element eo inside it.
-      const int rel = tok_ok ? vload(labels, t, g.T) - g.fw0 : -1;
+      const int rel = tok_ok ? lab[ci] - g.fw0 : -1;
       const int grp = rel >> 3, eo = rel & 7;
       const bool b0 = (eo & 1) != 0, b1 = (eo & 2) != 0, b2 = (eo & 4) != 0;
       float l[RI][2][8];
@@ -442,11 +463,18 @@ struct EpiCEBwd {
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
     const Lane L(g);
     const TileView<2> d(D, ldd, g.tw0, g.fw0);
+    int lab[CI];
+    float lsev[CI];
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
       const int t = g.tw0 + L.t(ci);
-      const int label = vload(labels, t, g.T) - g.fw0;
-      const float Lse = vload(lse, t, g.T);
+      lab[ci] = vload(labels, t, g.T);
+      lsev[ci] = vload(lse, t, g.T);
+    }
+#pragma unroll
+    for (int ci = 0; ci < CI; ++ci) {
+      const int label = lab[ci] - g.fw0;
+      const float Lse = lsev[ci];
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll

@@ -9,6 +9,7 @@
 // deterministic.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -114,26 +115,38 @@ __global__ void __launch_bounds__(RT) add_rmsnorm_kernel(const uint16_t* Y, int 
 // ---------------------------------------------------------------------------
 // RoPE (in place)
 // ---------------------------------------------------------------------------
+// One thread per 8-column chunk of the rotated range and group of rows: the
+// chunk's four frequencies are computed once and reused down the rows.  The
+// angle is reduced to revolutions and rotated with the hardware sine/cosine,
+// as in the fused epilogue.
+constexpr int ROPE_RC = 64, ROPE_RR = RT / ROPE_RC;  // chunks x rows per block
 __global__ void __launch_bounds__(RT) rope_kernel(uint16_t* __restrict__ Y, int ldy, const int32_t* __restrict__ pos,
-                                                  float log2_theta, int head_dim, int n_rope, float sgn, int M,
-                                                  int N) {
-  const long long n = nchunks(M, N), per = N / 8;
-  for (long long i = (long long)blockIdx.x * RT + threadIdx.x; i < n; i += (long long)gridDim.x * RT) {
-    const int row = (int)(i / per), c0 = (int)(i % per) * 8;
-    if (c0 >= n_rope) continue;
+                                                  float log2_theta, int head_dim, int n_rope, float sgn, int M) {
+  const int c0 = (blockIdx.x * ROPE_RC + (int)threadIdx.x % ROPE_RC) * 8;
+  if (c0 >= n_rope) return;
+  constexpr float INV_2PI = 0.15915494309189535f;
+  const float c_exp = log2_theta / (float)head_dim;
+  const int base = c0 % head_dim;
+  float fr[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    int j = base + 2 * q;  // (c0 + 2q) mod head_dim: head_dim >= 2 wraps at most three times
+    j -= j >= head_dim ? head_dim : 0;
+    j -= j >= head_dim ? head_dim : 0;
+    j -= j >= head_dim ? head_dim : 0;
+    fr[q] = exp2f(-(float)j * c_exp) * INV_2PI;
+  }
+  for (int row = blockIdx.y * ROPE_RR + (int)threadIdx.x / ROPE_RC; row < M; row += gridDim.y * ROPE_RR) {
     uint16_t* p = Y + (size_t)row * ldy + c0;
     float v[8];
     unpack8(ld16(p), v);
     const float ps = (float)pos[row];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int c = c0 + 2 * q;
-      if (c >= n_rope) break;
-      const int k = (c % head_dim) >> 1;
-      const float inv_freq = exp2f(-(float)(2 * k) / (float)head_dim * log2_theta);
-      float sn, cs;
-      sincosf(ps * inv_freq, &sn, &cs);
-      sn *= sgn;
+      if (c0 + 2 * q >= n_rope) break;
+      float rev = ps * fr[q];
+      rev -= floorf(rev);
+      const float sn = sgn * __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
       const float a = v[2 * q], b = v[2 * q + 1];
       v[2 * q] = a * cs - b * sn;
       v[2 * q + 1] = a * sn + b * cs;
@@ -389,8 +402,11 @@ coda_status coda_unfused_rope(coda_bf16* Y, int ldy, const int32_t* pos, float t
   if (c.st != CODA_OK) return c.st;
   if (M == 0 || N == 0 || n_rope == 0) return CODA_OK;
   if (coda_status s = device_ok()) return s;
-  hipLaunchKernelGGL(rope_kernel, dim3(grid_for(nchunks(M, N))), dim3(RT), 0, stream, Y, ldy, pos, log2f(theta),
-                     head_dim, n_rope, inverse ? -1.0f : 1.0f, M, N);
+  const int chunks = (n_rope + 7) / 8;
+  const int gx = (chunks + ROPE_RC - 1) / ROPE_RC;
+  const int gy = std::min((M + ROPE_RR - 1) / ROPE_RR, 16384);
+  hipLaunchKernelGGL(rope_kernel, dim3(gx, gy), dim3(RT), 0, stream, Y, ldy, pos, log2f(theta), head_dim, n_rope,
+                     inverse ? -1.0f : 1.0f, M);
   return launched();
 }
 

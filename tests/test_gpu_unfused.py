@@ -49,10 +49,12 @@ def test_unfused_add_rmsnorm(M, d, with_z):
     assert_close(f64(N2), n2, "N2")
 
 
-@pytest.mark.parametrize("inverse", [False, True])
-def test_unfused_rope(inverse):
-    M, N, hd, n_rope = 130, 384, 64, 256
-    say(f"case: unfused rope M={M} N={N} n_rope={n_rope} inverse={inverse}")
+@pytest.mark.parametrize("inverse,hd,n_rope", [(False, 64, 256), (True, 64, 256), (False, 2, 6), (True, 6, 18),
+                                                (False, 128, 384)])
+def test_unfused_rope(inverse, hd, n_rope):
+    """n_rope need not be a multiple of 8 here: the last chunk rotates only its leading pairs."""
+    M, N = 130, 384
+    say(f"case: unfused rope M={M} N={N} head_dim={hd} n_rope={n_rope} inverse={inverse}")
     t = S.normal_bf16(311, (M, N))
     pos = S.positions_int32(M, 2048)
     Y = dev(t)
