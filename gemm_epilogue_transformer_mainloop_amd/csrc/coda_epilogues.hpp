@@ -271,27 +271,59 @@ struct EpiRope {
           fr[ri][h][q] = f < n_rope ? w : 0.0f;
         }
       }
-#pragma unroll
-    for (int ci = 0; ci < CI; ++ci) {
+    // One 32-token column.  P = 0: the wave tile lies past n_rope (scale
+    // only).  Otherwise sine and cosine are evaluated for ri < P and reused
+    // for ri + P, ri + 2P, ...: the lane's features f and f + 32 P have the
+    // same angle when head_dim divides 32 P and the whole wave tile is
+    // rotated (head_dim 64: two heads per 128-feature wave tile, P = 2).
+    auto column = [&](int ci, auto p_c) {
+      constexpr int P = decltype(p_c)::value;
       const float rs = rsv[ci], ps = psv[ci];
+      float sn[P > 0 ? P : 1][2][4], cs[P > 0 ? P : 1][2][4];
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           float v[8];
           acc8(acc, ri, ci, h, v);
+          if constexpr (P == 0) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float rev = ps * fr[ri][h][q];
-            rev -= floorf(rev);
-            float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
-            if (INV) sn = -sn;
-            const float a = v[2 * q] * rs, b = v[2 * q + 1] * rs;
-            v[2 * q] = a * cs - b * sn;
-            v[2 * q + 1] = a * sn + b * cs;
+            for (int e = 0; e < 8; ++e) v[e] *= rs;
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (ri < P) {
+                float rev = ps * fr[ri][h][q];
+                rev -= floorf(rev);
+                sn[ri][h][q] = INV ? -__builtin_amdgcn_sinf(rev) : __builtin_amdgcn_sinf(rev);
+                cs[ri][h][q] = __builtin_amdgcn_cosf(rev);
+              }
+              const float sq = sn[ri % P][h][q], cq = cs[ri % P][h][q];
+              const float a = v[2 * q] * rs, b = v[2 * q + 1] * rs;
+              v[2 * q] = a * cq - b * sq;
+              v[2 * q + 1] = a * sq + b * cq;
+            }
           }
           y.store16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h), pack8(v));
         }
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using PR = std::integral_constant<int, RI>;
+    const bool whole = g.fw0 + 32 * RI <= n_rope;
+    if (g.fw0 >= n_rope) {
+#pragma unroll
+      for (int ci = 0; ci < CI; ++ci) column(ci, P0{});
+    } else if (whole && 32 % head_dim == 0) {
+#pragma unroll
+      for (int ci = 0; ci < CI; ++ci) column(ci, P1{});
+    } else if (whole && 64 % head_dim == 0) {
+#pragma unroll
+      for (int ci = 0; ci < CI; ++ci) column(ci, P2{});
+    } else {
+#pragma unroll
+      for (int ci = 0; ci < CI; ++ci) column(ci, PR{});
     }
   }
 };

@@ -44,7 +44,10 @@ def splits(F, T):
     return s
 
 
-def test_split_gemm_and_rope():
+@pytest.mark.parametrize("K", [8, 72, 136, 520])
+def test_split_gemm_and_rope(K):
+    """K = 8, 72, 136, 520: 1, 2, 3 and 9 k-tiles of 64 (the prologue and
+    tail cases of the half-tile k-loop, and its steady state)."""
     say(f"case: split gemm + rope M={M} N={N} K={K}")
     splits(N, M)
     A = S.normal_bf16(701, (M, K))
