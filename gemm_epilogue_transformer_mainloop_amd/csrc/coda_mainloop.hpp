@@ -314,15 +314,16 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
   constexpr int NRB = XK ? CI : 2 * CI;
   constexpr int NRD = NRA + NRB;
   constexpr int RPP = (NRD + NP - 1) / NP;
-  // Pairs of step 3 before the barrier.  0 (barrier at the start of step 3,
-  // once the step-3 fragments are read) lets the DMA of k-tile kt+2 spread
-  // over all 8 pairs: measured 7% fewer cycles per k-tile than 4.
-  constexpr int HP = 0;
-  constexpr int RPH = (NRD + (NP - HP) - 1) / (NP - HP);
   constexpr int NDMA = OA::NCH + OB::NCH;
-  constexpr int DPP = (NDMA + (NP - HP) - 1) / (NP - HP);
 
-  bf16x8 fa0[RI], fb0[CI], fa1[RI], fb1[CI];
+  // Fragments are read two k-steps ahead into four register sets (set s
+  // holds k-step s), so every fragment of a k-tile is in registers by the
+  // start of its step 2: the stage is released there and the DMA of k-tile
+  // kt+2 spreads over steps 2 and 3, DPE instructions per MFMA pair.  The
+  // texture unit takes about 57 B/clk per CU; one k-tile's 64 KiB of DMA
+  // issued within a single k-step (8 pairs) stalls the issuing waves.
+  bf16x8 fa0[RI], fb0[CI], fa1[RI], fb1[CI], fa2[RI], fb2[CI], fa3[RI], fb3[CI];
+  constexpr int DPE = (NDMA + 2 * NP - 1) / (2 * NP);
 
   // Read n (first-use order: a0, b0.., a1..) of k-step s from `stage` (0/1).
   // MN-major fragments take two transposing reads (n and n+1 of the same
@@ -402,13 +403,16 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
       __syncthreads();
 #pragma unroll
       for (int n = 0; n < NRD; ++n) read_one(0, 0, n, fa0, fb0);
+#pragma unroll
+      for (int n = 0; n < NRD; ++n) read_one(0, 1, n, fa1, fb1);
     }
 
-    // One k-tile: four k-steps of NP MFMA pairs, each pair carrying the
-    // fragment reads of the next k-step (other register set).  In step 3,
-    // after HP pairs: wait for k-tile kt+1's DMA, barrier, then the first
-    // fragment reads of k-tile kt+1 and the DMA of k-tile kt+2 into the stage
-    // k-tile kt has released.  sched_barrier fences keep the order.
+    // One k-tile: four k-steps of NP MFMA pairs.  Steps 0 and 1 carry the
+    // fragment reads of steps 2 and 3; then wait for k-tile kt+1's DMA and
+    // barrier (every wave holds all of k-tile kt's fragments, so its stage is
+    // free); steps 2 and 3 carry the fragment reads of k-tile kt+1's steps 0
+    // and 1 and the DMA of k-tile kt+2 into the released stage.
+    // sched_barrier fences keep the order.
     auto ktile = [&](int kt, auto has1_c, auto has2_c) {
       constexpr bool HAS1 = decltype(has1_c)::value, HAS2 = decltype(has2_c)::value;
       const int ST = kt & 1, NS = ST ^ 1;
@@ -416,41 +420,42 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
       for (int pr = 0; pr < NP; ++pr) {
         mfma_pair(fa0, fb0, pr);
 #pragma unroll
-        for (int r = 0; r < RPP; ++r) read_one(ST, 1, pr * RPP + r, fa1, fb1);
+        for (int r = 0; r < RPP; ++r) read_one(ST, 2, pr * RPP + r, fa2, fb2);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int pr = 0; pr < NP; ++pr) {
         mfma_pair(fa1, fb1, pr);
 #pragma unroll
-        for (int r = 0; r < RPP; ++r) read_one(ST, 2, pr * RPP + r, fa0, fb0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int pr = 0; pr < NP; ++pr) {
-        mfma_pair(fa0, fb0, pr);
-#pragma unroll
-        for (int r = 0; r < RPP; ++r) read_one(ST, 3, pr * RPP + r, fa1, fb1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int pr = 0; pr < HP; ++pr) {
-        mfma_pair(fa1, fb1, pr);
+        for (int r = 0; r < RPP; ++r) read_one(ST, 3, pr * RPP + r, fa3, fb3);
         __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (HAS1) wait_vmcnt<0>();
       __syncthreads();
       const int k2 = (kt + 2) * BK;
 #pragma unroll
-      for (int pr = HP; pr < NP; ++pr) {
-        mfma_pair(fa1, fb1, pr);
+      for (int pr = 0; pr < NP; ++pr) {
+        mfma_pair(fa2, fb2, pr);
         if constexpr (HAS1) {
 #pragma unroll
-          for (int r = 0; r < RPH; ++r) read_one(NS, 0, (pr - HP) * RPH + r, fa0, fb0);
+          for (int r = 0; r < RPP; ++r) read_one(NS, 0, pr * RPP + r, fa0, fb0);
         }
         if constexpr (HAS2) {
 #pragma unroll
-          for (int r = 0; r < DPP; ++r) dma(k2, ST, (pr - HP) * DPP + r);
+          for (int r = 0; r < DPE; ++r) dma(k2, ST, pr * DPE + r);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int pr = 0; pr < NP; ++pr) {
+        mfma_pair(fa3, fb3, pr);
+        if constexpr (HAS1) {
+#pragma unroll
+          for (int r = 0; r < RPP; ++r) read_one(NS, 1, pr * RPP + r, fa1, fb1);
+        }
+        if constexpr (HAS2) {
+#pragma unroll
+          for (int r = 0; r < DPE; ++r) dma(k2, ST, (NP + pr) * DPE + r);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
