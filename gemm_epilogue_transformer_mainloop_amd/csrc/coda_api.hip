@@ -127,18 +127,18 @@ coda_status launch_gemm_occ2(const uint16_t* W, int ldw, const uint16_t* X, int 
 // Tile-count quantization.  One 256x256 tile per CU at a time: when the tile
 // count leaves the last round of tiles partly empty (8192 x 3072 has 384
 // tiles = 1.5 rounds on 256 CUs), the trailing feature range can instead be
-// covered by 256-feature x 128-token tiles, which take about half as long and
-// come two per big tile.  Returns the number of 256-wide feature tiles to
-// keep in big tiles (the rest go to the half tiles), or 0 to keep every tile
-// big.  Cost model in rounds: a big round is 1, a half-tile round 0.55; a
-// split must save at least 0.2 rounds.
+// covered by 256-feature x 128-token tiles, two per big tile, each taking
+// about 0.6 of a big tile's time (measured on 8192 x 3072 x 2048).  Returns
+// the number of 256-wide feature tiles to keep in big tiles (the rest go to
+// the half tiles), or 0 to keep every tile big.  Cost model in rounds: a big
+// round is 1, a half-tile round 0.6; a split must save at least 0.2 rounds.
 inline int quantization_split(int nTF, int nTT, int nTT_half, int cus) {
   if (cus <= 0 || nTF < 2) return 0;
   const double base = (double)cdiv(nTF * nTT, cus);
   double best = base - 0.2;
   int split = 0;
   for (int f1 = 1; f1 < nTF; ++f1) {
-    const double c = (double)cdiv(f1 * nTT, cus) + 0.55 * (double)cdiv((nTF - f1) * nTT_half, cus);
+    const double c = (double)cdiv(f1 * nTT, cus) + 0.6 * (double)cdiv((nTF - f1) * nTT_half, cus);
     if (c < best) {
       best = c;
       split = f1;
@@ -175,11 +175,8 @@ coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, 
       half.f_base = split * BF;
       half.nTF = p.nTF - split;
       half.nTT = cdiv(T, 128);
-      hipLaunchKernelGGL((gemm_epi_kernel<BF, BT, WK, XK, Epi>), dim3(big.nTF * big.nTT), dim3(NT), 0, stream,
-                         big, epi);
-      if (hipPeekAtLastError() != hipSuccess) return launched();
-      hipLaunchKernelGGL((gemm_epi_kernel<BF, 128, WK, XK, Epi>), dim3(half.nTF * half.nTT), dim3(NT), 0,
-                         stream, half, epi);
+      hipLaunchKernelGGL((gemm_epi_kernel_split<WK, XK, Epi>), dim3(big.nTF * big.nTT + half.nTF * half.nTT),
+                         dim3(NT), 0, stream, big, half, epi);
       return launched();
     }
   }

@@ -264,8 +264,16 @@ __device__ __forceinline__ void tile_coords(int bid, int nb, int nTF, int nTT, i
 // The kernel
 // ---------------------------------------------------------------------------
 
+// LDS bytes of one workgroup: two stages of both operand tiles.
+template <int BF, int BT, bool WK, bool XK>
+constexpr int lds_bytes() {
+  return 2 * (Operand<BF, WK>::REGION + Operand<BT, XK>::REGION);
+}
+
+// One BF x BT output tile: block `bid` of `nb` blocks working on problem p,
+// with the workgroup's LDS at `smem` (lds_bytes<BF, BT, WK, XK>() bytes).
 template <int BF, int BT, bool WK, bool XK, class Epi>
-__global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi epi) {
+__device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, char* smem, int bid, int nb) {
   static_assert(BF == 256 && (BT == 256 || BT == 128), "tile shape");
   constexpr int WGF = 2, WGT = 2;           // 2 x 2 waves
   constexpr int WF = BF / WGF, WT = BT / WGT;
@@ -273,17 +281,15 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
   constexpr int RI = WF / 32, CI = WT / 32;
   using OA = Operand<BF, WK>;
   using OB = Operand<BT, XK>;
-  // LDS: A stage 0 | A stage 1 | B stage 0 | B stage 1 (stage bit = bit 15 or 14)
+  // LDS: A stage 0 | A stage 1 | B stage 0 | B stage 1
   constexpr int A_REG = OA::REGION, B_REG = OB::REGION, B_OFF = 2 * A_REG;
-
-  __shared__ __attribute__((aligned(1024))) char smem[2 * (A_REG + B_REG)];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf = wave % WGF, wt = wave / WGF;
   const int lt = lane & 31, hh = lane >> 5;
   int tf, tt;
-  tile_coords(blockIdx.x, gridDim.x, p.nTF, p.nTT, tf, tt);
+  tile_coords(bid, nb, p.nTF, p.nTT, tf, tt);
   const int f0 = p.f_base + tf * BF, t0 = tt * BT;
 
   f32x16 acc[RI][CI];
@@ -488,6 +494,26 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
   g.pf = g.fw0 / WAVE_F;
   g.pt = g.tw0 / WT;
   epi.template apply<RI, CI>(acc, g);
+}
+
+template <int BF, int BT, bool WK, bool XK, class Epi>
+__global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi epi) {
+  __shared__ __attribute__((aligned(1024))) char smem[lds_bytes<BF, BT, WK, XK>()];
+  gemm_epi_tile<BF, BT, WK, XK, Epi>(p, epi, smem, blockIdx.x, gridDim.x);
+}
+
+// Two tile shapes in one dispatch (tile-count split): blocks [0, nbig) cover
+// problem p in 256 x 256 tiles, the others cover q (the trailing features) in
+// 256 x 128 tiles; the hardware dispatches those as the first ones finish.
+template <bool WK, bool XK, class Epi>
+__global__ void __launch_bounds__(NT) gemm_epi_kernel_split(const Problem p, const Problem q, const Epi epi) {
+  constexpr int BIG = lds_bytes<256, 256, WK, XK>(), HALF = lds_bytes<256, 128, WK, XK>();
+  __shared__ __attribute__((aligned(1024))) char smem[BIG > HALF ? BIG : HALF];
+  const int nbig = p.nTF * p.nTT;
+  if ((int)blockIdx.x < nbig)
+    gemm_epi_tile<256, 256, WK, XK, Epi>(p, epi, smem, blockIdx.x, nbig);
+  else
+    gemm_epi_tile<256, 128, WK, XK, Epi>(q, epi, smem, blockIdx.x - nbig, gridDim.x - nbig);
 }
 
 }  // namespace coda

@@ -70,7 +70,7 @@ int coda_mparts(int M);
  * and T tokens (M) on a device with `cus` compute units.  Output tiles are
  * 256 features x 256 tokens, one per compute unit at a time; when that
  * leaves the last round of tiles mostly empty, the features from
- * 256 * split on are computed in 256 x 128 tiles in a second launch.
+ * 256 * split on are computed in 256 x 128 tiles by the same dispatch.
  * Returns split (0: all tiles 256 x 256).  Applies to coda_gemm, the forward
  * calls, coda_gemm_swiglu_bwd, coda_gemm_res_sumsq_bwd (dX) and the GEMMs
  * of the LM head; coda_gemm_rowscale_bwd and the weight gradients always use

@@ -79,7 +79,7 @@ def test_tile_split(L):
             base = -(-nF * nT // cus2)
             if s:
                 assert 0 < s < nF
-                cost = -(-s * nT // cus2) + 0.55 * -(-(nF - s) * 64 // cus2)
+                cost = -(-s * nT // cus2) + 0.6 * -(-(nF - s) * 64 // cus2)
                 assert cost <= base - 0.2
 
 
@@ -178,8 +178,9 @@ def test_no_kernel_spills():
     for name, v in res.items():
         assert v["scratch"] == 0 and v["vgpr_spill"] == 0, name
     # the main loop holds the 128x128 wave tile in the 256 accumulation
-    # registers; the 256x128-tile kernels (tile-count split) hold 128x64
-    half = {k: v for k, v in gemm.items() if "ILi256ELi128E" in k}
-    assert half, "no 256x128-tile kernels"
-    assert all(v["agprs"] == 256 for k, v in gemm.items() if k not in half)
-    assert all(v["agprs"] == 128 for v in half.values())
+    # registers (also in the tile-count split kernels, whose second tile
+    # shape, 256x128, holds 128x64)
+    split = [k for k in gemm if "gemm_epi_kernel_split" in k]
+    assert split, "no tile-count split kernels"
+    assert all(v["agprs"] == 256 for v in gemm.values())
+    assert all(v["lds"] <= 160 * 1024 for v in res.values())
