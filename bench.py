@@ -619,32 +619,44 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    tm = OpTimer(torch)
+    # The timed region holds the K steps and nothing else: a HIP event per
+    # call would add GPU work between the kernels.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for _ in range(args.steps):
-        step(tm)
+        step()
     t_end.record()
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
+
+    # Per-op breakdown (and the roofline kernel's time): another K steps with
+    # an event pair around every call, outside the timed region.
+    tm = OpTimer(torch)
+    for _ in range(args.steps):
+        step(tm)
+    torch.cuda.synchronize()
     op_ms = tm.mean_ms()
     op_stats = tm.stats_ms()
 
-    # The unfused sequence of the same block, same inputs, same number of steps.
+    # The unfused sequence of the same block, same inputs, same number of
+    # steps, timed the same way.
     ustep = make_c2_unfused_step(torch, coda, T, dims, p["eps"], n_rope)
     for _ in range(args.warmup):
         ustep()
-    utm = OpTimer(torch)
     torch.cuda.synchronize()
     t_start.record()
     for _ in range(args.steps):
-        ustep(utm)
+        ustep()
     t_end.record()
     torch.cuda.synchronize()
     ums_step = t_start.elapsed_time(t_end) / args.steps
+    utm = OpTimer(torch)
+    for _ in range(args.steps):
+        ustep(utm)
+    torch.cuda.synchronize()
     uops = {k: {"us_median": round(v[1] * 1e3, 2), "us_min": round(v[2] * 1e3, 2)}
             for k, v in utm.stats_ms().items()}
     log(f"unfused sequence: {ums_step * 1e3:.1f} us/step  {uops}")
