@@ -150,7 +150,7 @@ inline int quantization_split(int nTF, int nTT, int nTT_half, int cus) {
 template <bool WK, bool XK, int BT = 256, class Epi>
 coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, int F, int T, int K,
                         const Epi& epi, hipStream_t stream) {
-  if constexpr (CODA_OCC2 && XK && AnyWaveWidth<Epi>::value) {
+  if constexpr (CODA_OCC2 && XK && AnyWaveWidth<Epi>::value && EpiLds<Epi>::value == 0) {
     return launch_gemm_occ2<WK>(W, ldw, X, ldx, F, T, K, epi, stream);
   }
   constexpr int BF = 256;

@@ -122,6 +122,9 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t range, uint32_t
 
 // s_waitcnt vmcnt(N), other counters unconstrained (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+// s_waitcnt lgkmcnt(0), other counters unconstrained.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt");
@@ -263,6 +266,13 @@ __device__ __forceinline__ void tile_coords(int bid, int nb, int nTF, int nTT, i
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
+
+// LDS bytes an epilogue stages its tile I/O through after the main loop
+// (Epi::LDS_BYTES; 0 for epilogues that work from registers alone).
+template <class E, class = void>
+struct EpiLds : std::integral_constant<int, 0> {};
+template <class E>
+struct EpiLds<E, std::void_t<decltype(E::LDS_BYTES)>> : std::integral_constant<int, E::LDS_BYTES> {};
 
 // LDS bytes of one workgroup: two stages of both operand tiles.
 template <int BF, int BT, bool WK, bool XK>
@@ -493,11 +503,17 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
   g.T = p.T;
   g.pf = g.fw0 / WAVE_F;
   g.pt = g.tw0 / WT;
-  epi.template apply<RI, CI>(acc, g);
+  if constexpr (EpiLds<Epi>::value > 0) {
+    __syncthreads();  // every wave is done with the operand stages
+    epi.template apply<RI, CI>(acc, g, smem);
+  } else {
+    epi.template apply<RI, CI>(acc, g);
+  }
 }
 
 template <int BF, int BT, bool WK, bool XK, class Epi>
 __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi epi) {
+  static_assert(EpiLds<Epi>::value <= lds_bytes<BF, BT, WK, XK>(), "epilogue staging exceeds the LDS");
   __shared__ __attribute__((aligned(1024))) char smem[lds_bytes<BF, BT, WK, XK>()];
   gemm_epi_tile<BF, BT, WK, XK, Epi>(p, epi, smem, blockIdx.x, gridDim.x);
 }
@@ -508,6 +524,7 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
 template <bool WK, bool XK, class Epi>
 __global__ void __launch_bounds__(NT) gemm_epi_kernel_split(const Problem p, const Problem q, const Epi epi) {
   constexpr int BIG = lds_bytes<256, 256, WK, XK>(), HALF = lds_bytes<256, 128, WK, XK>();
+  static_assert(EpiLds<Epi>::value <= (BIG > HALF ? BIG : HALF), "epilogue staging exceeds the LDS");
   __shared__ __attribute__((aligned(1024))) char smem[BIG > HALF ? BIG : HALF];
   const int nbig = p.nTF * p.nTT;
   if ((int)blockIdx.x < nbig)
