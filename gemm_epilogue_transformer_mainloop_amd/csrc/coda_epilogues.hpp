@@ -88,6 +88,42 @@ __device__ __forceinline__ void acc8(const f32x16 (&acc)[RI][CI], int ri, int ci
   for (int e = 0; e < 8; ++e) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[e]) : "a"(acc[ri][ci][8 * half + e]));
 }
 
+// A wave's bf16 output tile (CI x 32 tokens x 128 features) staged through
+// the wave's 32 KiB slice of the LDS the main loop has released.  put()
+// writes one lane-layout run (8 features of one token); flush() reads whole
+// rows back and stores each as one 256-byte segment, four rows per
+// instruction, so global stores cover whole rows instead of 16-byte pieces
+// of 32 rows.  Chunk c (8 features) of row r sits at position c ^ (r & 15):
+// both access patterns are free of bank conflicts.  Writes and reads are
+// the same wave's, which the LDS serves in order.
+constexpr int STAGE_LDS = 4 * 32768;  // bytes for the four waves
+
+struct Stage {
+  char* reg;
+  __device__ __forceinline__ explicit Stage(char* smem)
+      : reg(smem + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * 32768) {}
+  __device__ __forceinline__ void put(const Geom& g, int ci, int ri, int h, u32x4 v) const {
+    const int r = ci * 32 + g.lt, c = 4 * ri + 2 * h + g.hh;
+    st16(reg + r * 256 + ((c ^ (r & 15)) << 4), v);
+  }
+  template <int CI>
+  __device__ __forceinline__ void flush(const Geom& g, const TileView<2>& out) const {
+    const int T = g.T - g.tw0, F = g.F - g.fw0;
+    const int rlo = g.lane >> 4, pos = g.lane & 15;
+#pragma unroll
+    for (int i0 = 0; i0 < CI * 8; i0 += 8) {
+      u32x4 sv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sv[i] = ld16(reg + (i0 + i) * 1024 + 16 * g.lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * (i0 + i) + rlo, c = pos ^ (r & 15);
+        out.store16(r, 8 * c, r < T && 8 * c < F, sv[i]);
+      }
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Store-only / row-scale / residual epilogue:  Y = bf16( r_t * acc + res )
 // (plain GEMM; GEMM2's delayed RMSNorm scale; data-gradient + residual)
@@ -100,9 +136,12 @@ struct EpiLinear {
   uint16_t* Y;
   int ldy;
 
+  static constexpr int LDS_BYTES = STAGE_LDS;
+
   template <int RI, int CI>
-  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g, char* smem) const {
     const Lane L(g);
+    const Stage stage(smem);
     const TileView<2> y(Y, ldy, g.tw0, g.fw0);
     float rsv[CI];
 #pragma unroll
@@ -134,9 +173,10 @@ struct EpiLinear {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] += z[e];
           }
-          y.store16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h), pack8(v));
+          stage.put(g, ci, ri, h, pack8(v));
         }
     }
+    stage.flush<CI>(g, y);
   }
 };
 
@@ -157,9 +197,14 @@ struct EpiResSumsq {
   float* part;
   int nparts;
 
+  static constexpr int LDS_BYTES = STAGE_LDS;
+
+  // u goes out through the LDS stage (whole-row stores); h2, formed from the
+  // same unrounded u, is stored directly.
   template <int RI, int CI>
-  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g, char* smem) const {
     const Lane L(g);
+    const Stage stage(smem);
     const TileView<2> uo(U, ldu, g.tw0, g.fw0);
     u32x4 gv[RI][2];
     if constexpr (HAS_H2) {
@@ -168,22 +213,29 @@ struct EpiResSumsq {
 #pragma unroll
         for (int h = 0; h < 2; ++h) gv[ri][h] = vload16_bf16(gamma, g.fw0 + L.f(ri, h), g.F);
     }
-    // z is double-buffered per 32-token column (loads of column ci+1 are in
-    // flight while column ci is computed and stored).
+    // The wave's whole z tile, loaded before anything else is stored.
     const TileView<2> zi(z, ldz, g.tw0, g.fw0);
-    u32x4 zv[2][RI][2];
-    auto load_col = [&](int ci, u32x4 (&b)[RI][2]) {
+    u32x4 zv[CI][RI][2];
+    if constexpr (HAS_Z) {
 #pragma unroll
-      for (int ri = 0; ri < RI; ++ri)
+      for (int ci = 0; ci < CI; ++ci)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) b[ri][h] = zi.load16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h));
+        for (int ri = 0; ri < RI; ++ri)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) zv[ci][ri][h] = zi.load16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h));
+    }
+    auto u8 = [&](int ci, int ri, int h, float (&v)[8]) {
+      acc8(acc, ri, ci, h, v);
+      if constexpr (HAS_Z) {
+        float zz[8];
+        unpack8(zv[ci][ri][h], zz);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += zz[e];
+      }
     };
-    if constexpr (HAS_Z) load_col(0, zv[0]);
+    const TileView<2> ho(H2, ldh, g.tw0, g.fw0);
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
-      if constexpr (HAS_Z) {
-        if (ci + 1 < CI) load_col(ci + 1, zv[(ci + 1) & 1]);
-      }
       float ss = 0.0f;
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
@@ -191,14 +243,8 @@ struct EpiResSumsq {
         for (int h = 0; h < 2; ++h) {
           const bool ok = L.ok(ci, ri, h);
           float v[8];
-          acc8(acc, ri, ci, h, v);
-          if constexpr (HAS_Z) {
-            float zz[8];
-            unpack8(zv[ci & 1][ri][h], zz);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] += zz[e];
-          }
-          uo.store16(L.t(ci), L.f(ri, h), ok, pack8(v));
+          u8(ci, ri, h, v);
+          stage.put(g, ci, ri, h, pack8(v));
           float sq = 0.0f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) sq += v[e] * v[e];
@@ -208,7 +254,6 @@ struct EpiResSumsq {
             unpack8(gv[ri][h], gm);
 #pragma unroll
             for (int e = 0; e < 8; ++e) hv[e] = v[e] * gm[e];
-            const TileView<2> ho(H2, ldh, g.tw0, g.fw0);
             ho.store16(L.t(ci), L.f(ri, h), ok, pack8(hv));
           }
         }
@@ -219,6 +264,7 @@ struct EpiResSumsq {
         if (w) part[(size_t)t * nparts + g.pf] = ss;
       }
     }
+    stage.flush<CI>(g, uo);
   }
 };
 
@@ -237,9 +283,12 @@ struct EpiRope {
   uint16_t* Y;
   int ldy;
 
+  static constexpr int LDS_BYTES = STAGE_LDS;
+
   template <int RI, int CI>
-  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g, char* smem) const {
     const Lane L(g);
+    const Stage stage(smem);
     const TileView<2> y(Y, ldy, g.tw0, g.fw0);
     float rsv[CI], psv[CI];
 #pragma unroll
@@ -304,7 +353,7 @@ struct EpiRope {
               v[2 * q + 1] = a * sq + b * cq;
             }
           }
-          y.store16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h), pack8(v));
+          stage.put(g, ci, ri, h, pack8(v));
         }
     };
     using P0 = std::integral_constant<int, 0>;
@@ -325,6 +374,7 @@ struct EpiRope {
 #pragma unroll
       for (int ci = 0; ci < CI; ++ci) column(ci, PR{});
     }
+    stage.flush<CI>(g, y);
   }
 };
 
@@ -341,8 +391,10 @@ struct EpiSwiglu {
   uint16_t* pre;
   int ldp;
 
+  static constexpr int LDS_BYTES = HAS_PRE ? STAGE_LDS : 0;
+
   template <int RI, int CI>
-  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g, char* smem = nullptr) const {
     const Lane L(g);
     const TileView<2> ao(act, ldact, g.tw0, g.fw0 >> 1);
     const TileView<2> po(pre, ldp, g.tw0, g.fw0);
@@ -369,7 +421,7 @@ struct EpiSwiglu {
             a[q] = gg * sigmoidf_(gg) * uu;
           }
           ah[h] = (u32x2){pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-          if constexpr (HAS_PRE) po.store16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h), pack8(v));
+          if constexpr (HAS_PRE) Stage(smem).put(g, ci, ri, h, pack8(v));
         }
         // Exchange with lane l ^ 32 so that each lane holds 8 consecutive
         // a-columns (16 ri + 8 hh + 0..7) and writes them with one 16-byte store.
@@ -386,6 +438,7 @@ struct EpiSwiglu {
         ao.store8(L.t(ci), ri * 16 + g.hh * 8, half, (u32x2){out[0], out[1]});
       }
     }
+    if constexpr (HAS_PRE) Stage(smem).flush<CI>(g, po);
   }
 };
 
