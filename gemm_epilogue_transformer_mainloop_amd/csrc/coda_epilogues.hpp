@@ -544,9 +544,12 @@ struct EpiCEBwd {
   uint16_t* D;
   int ldd;
 
+  static constexpr int LDS_BYTES = STAGE_LDS;
+
   template <int RI, int CI>
-  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g, char* smem) const {
     const Lane L(g);
+    const Stage stage(smem);
     const TileView<2> d(D, ldd, g.tw0, g.fw0);
     int lab[CI];
     float lsev[CI];
@@ -571,9 +574,10 @@ struct EpiCEBwd {
             const float pr = fast_exp(v[e] - Lse);
             v[e] = (pr - (label == L.f(ri, h) + e ? 1.0f : 0.0f)) * scale;
           }
-          d.store16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h), pack8(v));
+          stage.put(g, ci, ri, h, pack8(v));
         }
     }
+    stage.flush<CI>(g, d);
   }
 };
 
@@ -812,10 +816,50 @@ struct EpiF32 {
   float* out;
   int ld;
 
+  // The plain store goes through the released LDS (fp32 rows of 512 bytes,
+  // 64 rows per 32 KiB wave slice, so two passes of two 32-token columns);
+  // the accumulating form keeps its register path.
+  static constexpr int LDS_BYTES = ACCUM ? 0 : STAGE_LDS;
+
   template <int RI, int CI>
-  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g, char* smem = nullptr) const {
     const Lane L(g);
     const TileView<4> o(out, ld, g.tw0, g.fw0);
+    if constexpr (!ACCUM) {
+      static_assert(CI % 2 == 0, "passes of two 32-token columns");
+      char* reg = smem + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * 32768;
+      const int rlo = g.lane >> 5, pos = g.lane & 31;
+#pragma unroll
+      for (int p = 0; p < CI / 2; ++p) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const int ci = 2 * p + cc, r = 32 * cc + g.lt;
+#pragma unroll
+          for (int ri = 0; ri < RI; ++ri)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int c = 0; c < 2; ++c) {  // chunk = 4 consecutive features
+                const f32x4 v = {acc[ri][ci][8 * h + 4 * c + 0], acc[ri][ci][8 * h + 4 * c + 1],
+                                 acc[ri][ci][8 * h + 4 * c + 2], acc[ri][ci][8 * h + 4 * c + 3]};
+                const int chunk = 8 * ri + 4 * h + 2 * g.hh + c;
+                st16(reg + r * 512 + ((chunk ^ (r & 7)) << 4), __builtin_bit_cast(u32x4, v));
+              }
+        }
+#pragma unroll
+        for (int i0 = 0; i0 < 32; i0 += 8) {
+          u32x4 sv[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sv[i] = ld16(reg + (i0 + i) * 1024 + 16 * g.lane);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int r = 2 * (i0 + i) + rlo, c = pos ^ (r & 7);
+            o.store16(64 * p + r, 4 * c, 64 * p + r < L.T && 4 * c < L.F, sv[i]);
+          }
+        }
+      }
+      return;
+    }
     u32x4 prev[2][RI][2][2];
     auto load_col = [&](int ci, u32x4 (&b)[RI][2][2]) {
 #pragma unroll
