@@ -22,58 +22,115 @@ using namespace coda_host;
 namespace {
 
 // ---------------------------------------------------------------------------
-// Auxiliary reductions (fixed order, one thread per output element)
+// Auxiliary reductions.  Bandwidth/latency-bound: every load instruction of a
+// wave reads contiguous floats, the summation order is fixed (deterministic).
 // ---------------------------------------------------------------------------
 
-// r_i = 1/sqrt(sum_p part[i,p]/d + eps)  (paper Figure 4 / Figure 5 caption)
-__global__ void row_rms_kernel(const float* __restrict__ part, int nparts, int M, float inv_d,
-                               float eps, float* __restrict__ r) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= M) return;
-  const float* p = part + (size_t)i * nparts;
+// Row sums of per-row partials [M x nparts] (row-major, ld = nparts), G lanes
+// per row: lane k adds elements k, k+G, ..., then a butterfly over the G lanes.
+// RMS: out_i = 1/sqrt(sum/d + eps) (paper Figure 4 / Figure 5 caption);
+// otherwise out_i = sum/d (the backward statistic s, reading notes section 3).
+template <int G, bool RMS>
+__global__ void __launch_bounds__(256) row_reduce_kernel(const float* __restrict__ part, int nparts,
+                                                         int M, float inv_d, float eps,
+                                                         float* __restrict__ out) {
+  const int row = blockIdx.x * (256 / G) + (int)threadIdx.x / G;
+  const int k = (int)threadIdx.x % G;
   float s = 0.0f;
-  for (int j = 0; j < nparts; ++j) s += p[j];
-  r[i] = 1.0f / sqrtf(s * inv_d + eps);
+  if (row < M) {
+    const float* p = part + (size_t)row * nparts;
+#pragma unroll 4
+    for (int j = k; j < nparts; j += G) s += p[j];
+  }
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (row < M && k == 0) out[row] = RMS ? 1.0f / sqrtf(s * inv_d + eps) : s * inv_d;
 }
 
-// s_i = sum_p spart[i,p] / d  (reading notes section 3)
-__global__ void row_sum_scale_kernel(const float* __restrict__ part, int nparts, int M, float inv_d,
-                                     float* __restrict__ out) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= M) return;
-  const float* p = part + (size_t)i * nparts;
-  float s = 0.0f;
-  for (int j = 0; j < nparts; ++j) s += p[j];
-  out[i] = s * inv_d;
+template <bool RMS>
+void launch_row_reduce(const float* part, int nparts, int M, float inv_d, float eps, float* out,
+                       hipStream_t stream) {
+  if (nparts <= 4)
+    hipLaunchKernelGGL((row_reduce_kernel<4, RMS>), dim3(cdiv(M, 64)), dim3(256), 0, stream, part,
+                       nparts, M, inv_d, eps, out);
+  else if (nparts <= 16)
+    hipLaunchKernelGGL((row_reduce_kernel<16, RMS>), dim3(cdiv(M, 16)), dim3(256), 0, stream, part,
+                       nparts, M, inv_d, eps, out);
+  else
+    hipLaunchKernelGGL((row_reduce_kernel<64, RMS>), dim3(cdiv(M, 4)), dim3(256), 0, stream, part,
+                       nparts, M, inv_d, eps, out);
 }
 
-// dgamma_j = sum_q gpart[q, j]
-__global__ void col_reduce_kernel(const float* __restrict__ gpart, int mparts, int d,
-                                  float* __restrict__ out) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= d) return;
+// dgamma_j = sum_q gpart[q, j]: a workgroup takes 32 columns, its eight
+// waves-halves take every eighth partial row, and the eight slice sums are
+// added in a fixed order.
+constexpr int CR_COLS = 32, CR_SLICES = 8;
+__global__ void __launch_bounds__(256) col_reduce_kernel(const float* __restrict__ gpart, int mparts,
+                                                         int d, float* __restrict__ out) {
+  __shared__ float sh[CR_SLICES][CR_COLS];
+  const int c = (int)threadIdx.x % CR_COLS, sl = (int)threadIdx.x / CR_COLS;
+  const int j = blockIdx.x * CR_COLS + c;
   float s = 0.0f;
-  for (int q = 0; q < mparts; ++q) s += gpart[(size_t)q * d + j];
-  out[j] = s;
+  if (j < d) {
+#pragma unroll 4
+    for (int q = sl; q < mparts; q += CR_SLICES) s += gpart[(size_t)q * d + j];
+  }
+  sh[sl][c] = s;
+  __syncthreads();
+  if (sl == 0 && j < d) {
+    float t = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CR_SLICES; ++k) t += sh[k][c];
+    out[j] = t;
+  }
 }
 
-// Merge of per-tile (max, sum exp) into lse and the row loss (notes sec. 2).
-// Partials are part-major ([nparts x M]): consecutive threads read
-// consecutive tokens.
-__global__ void ce_reduce_kernel(const float* __restrict__ pm, const float* __restrict__ ps,
-                                 const float* __restrict__ tgt, const int32_t* __restrict__ labels,
-                                 int nparts, int M, int V, float* __restrict__ lse,
-                                 float* __restrict__ loss) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= M) return;
-  float L = -INFINITY;
-  for (int j = 0; j < nparts; ++j) L = fmaxf(L, pm[(size_t)j * M + i]);
-  float S = 0.0f;
-  for (int j = 0; j < nparts; ++j) S += ps[(size_t)j * M + i] * expf(pm[(size_t)j * M + i] - L);
-  const float l = L + logf(S);
-  lse[i] = l;
-  const int y = labels[i];
-  loss[i] = (y >= 0 && y < V) ? (l - tgt[i]) : __builtin_nanf("");
+// Merge of per-tile (max, sum exp) into lse and the row loss (reading notes
+// section 2, "Cross-entropy loss").  Partials are part-major ([nparts x ldp]).
+// A workgroup takes 32 tokens; each of its 32 slices merges every 32nd part
+// with one exponential per part (the smaller of the two maxima is rescaled),
+// and the 32 slice states of a token are merged in a fixed order.
+constexpr int CE_TOK = 32, CE_SLICES = 32;
+__global__ void __launch_bounds__(1024) ce_reduce_kernel(const float* __restrict__ pm,
+                                                         const float* __restrict__ ps,
+                                                         const float* __restrict__ tgt,
+                                                         const int32_t* __restrict__ labels,
+                                                         int nparts, int M, int ldp, int V,
+                                                         float* __restrict__ lse,
+                                                         float* __restrict__ loss) {
+  __shared__ float shm[CE_SLICES][CE_TOK], shs[CE_SLICES][CE_TOK];
+  const int tl = (int)threadIdx.x % CE_TOK, sl = (int)threadIdx.x / CE_TOK;
+  const int i = blockIdx.x * CE_TOK + tl;
+  float m = -INFINITY, s = 0.0f;
+  if (i < M) {
+#pragma unroll 4
+    for (int j = sl; j < nparts; j += CE_SLICES) {
+      const float a = pm[(size_t)j * ldp + i], b = ps[(size_t)j * ldp + i];
+      if (a > -INFINITY) {
+        const float dl = a - m;
+        const bool up = dl > 0.0f;
+        const float e = expf(-fabsf(dl));
+        s = up ? fmaf(s, e, b) : fmaf(b, e, s);
+        m = up ? a : m;
+      }
+    }
+  }
+  shm[sl][tl] = m;
+  shs[sl][tl] = s;
+  __syncthreads();
+  if (sl == 0 && i < M) {
+    float L = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < CE_SLICES; ++k) L = fmaxf(L, shm[k][tl]);
+    float S = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CE_SLICES; ++k)
+      S += shm[k][tl] > -INFINITY ? shs[k][tl] * expf(shm[k][tl] - L) : 0.0f;
+    const float l = L + logf(S);
+    lse[i] = l;
+    const int y = labels[i];
+    loss[i] = (y >= 0 && y < V) ? (l - tgt[i]) : __builtin_nanf("");
+  }
 }
 
 // Deterministic mean of the row losses: one workgroup, fixed-order tree.
@@ -288,8 +345,7 @@ coda_status coda_row_rms(const float* part, int nparts, int M, int d, float eps,
   if (c.st != CODA_OK) return c.st;
   if (M == 0) return CODA_OK;
   if (coda_status s = device_ok()) return s;
-  hipLaunchKernelGGL(row_rms_kernel, dim3(cdiv(M, 256)), dim3(256), 0, stream, part, nparts, M,
-                     1.0f / (float)d, eps, r);
+  launch_row_reduce<true>(part, nparts, M, 1.0f / (float)d, eps, r, stream);
   return launched();
 }
 
@@ -411,8 +467,8 @@ coda_status coda_lmhead_ce(const coda_bf16* H, int ldh, const coda_bf16* W, int 
   if (loss_row == nullptr) loss_row = lrow;
   EpiCE e{labels, pm, ps, tgt, M};
   if (coda_status s = launch_gemm<false, true>(W, ldw, H, ldh, V, M, d, e, stream)) return s;
-  hipLaunchKernelGGL(ce_reduce_kernel, dim3(cdiv(M, 256)), dim3(256), 0, stream, pm, ps, tgt,
-                     labels, np, M, V, lse, loss_row);
+  hipLaunchKernelGGL(ce_reduce_kernel, dim3(cdiv(M, CE_TOK)), dim3(CE_TOK * CE_SLICES), 0, stream,
+                     pm, ps, tgt, labels, np, M, M, V, lse, loss_row);
   if (coda_status s = launched()) return s;
   if (loss_mean) {
     hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, stream, loss_row, M, loss_mean);
@@ -455,8 +511,7 @@ coda_status coda_row_rms_bwd(const float* spart, int nparts, int M, int d, float
   if (c.st != CODA_OK) return c.st;
   if (M == 0) return CODA_OK;
   if (coda_status st = device_ok()) return st;
-  hipLaunchKernelGGL(row_sum_scale_kernel, dim3(cdiv(M, 256)), dim3(256), 0, stream, spart,
-                     nparts, M, 1.0f / (float)d, s);
+  launch_row_reduce<false>(spart, nparts, M, 1.0f / (float)d, 0.0f, s, stream);
   return launched();
 }
 
@@ -508,8 +563,8 @@ coda_status coda_col_reduce(const float* gpart, int mparts, int d, float* dgamma
   if (c.st != CODA_OK) return c.st;
   if (d == 0) return CODA_OK;
   if (coda_status st = device_ok()) return st;
-  hipLaunchKernelGGL(col_reduce_kernel, dim3(cdiv(d, 256)), dim3(256), 0, stream, gpart, mparts, d,
-                     dgamma);
+  hipLaunchKernelGGL(col_reduce_kernel, dim3(cdiv(d, CR_COLS)), dim3(256), 0, stream, gpart, mparts,
+                     d, dgamma);
   return launched();
 }
 
