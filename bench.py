@@ -319,7 +319,18 @@ def bench_all(torch, coda, synth, iters=20):
     ent["pct_peak"] = 100 * ent["tflops"] / PEAK_BF16_TFLOPS
     rows.append(ent)
     log(json.dumps(ent))
-    del h, W, ws, wsb, dH, dW
+    del wsb
+    L = torch.empty(M, V, dtype=bf, device="cuda")
+    rec(4, "lmhead_ce_logits", M, V, d, lambda: coda.coda_lmhead_ce_logits(h, W, labels, lse, lr, lm, L, ws),
+        plain_nn(M, V, d))
+    # each timed call turns the buffer's dlogits into dlogits again: same work
+    med, mn = time_fn(torch, lambda: coda.coda_lmhead_ce_bwd_logits(h, W, labels, lse, 1.0 / M, L, dH, dW), 5, 2)
+    ent = {"config": 4, "op": "lmhead_ce_bwd_logits (dlogits + 2 GEMMs)", "M": M, "N": V, "K": d,
+           "us_median": med * 1e3, "tflops": 2 * 2.0 * M * V * d / (med * 1e-3) / 1e12}
+    ent["pct_peak"] = 100 * ent["tflops"] / PEAK_BF16_TFLOPS
+    rows.append(ent)
+    log(json.dumps(ent))
+    del h, W, ws, L, dH, dW
     # config 5: the block-backward fused calls at 8B-like shape
     M, d, F = 8192, 4096, 14336
     dOut, Wd, Wgu = rnd(M, d), rnd(F, d, std=F ** -0.5), rnd(d, 2 * F, std=d ** -0.5)
@@ -454,7 +465,14 @@ def bench_sequences(torch, coda, iters=20):
     # algorithmic work: the forward GEMM and the two gradient GEMMs (the fused
     # backward's logit recomputation is not counted)
     seq(4, "LM head + CE forward+backward", 3 * 2.0 * M * d * V, f_ce_bwd, u_ce_bwd, 3)
-    del h, W, ws, wsb, L, dH, dW
+
+    def f_ce_bwd_logits():
+        coda.coda_lmhead_ce_logits(h, W, labels, lse, lr, lm, L, ws)
+        coda.coda_lmhead_ce_bwd_logits(h, W, labels, lse, 1.0 / M, L, dH, dW)
+
+    del wsb
+    seq(4, "LM head + CE forward+backward, stored logits", 3 * 2.0 * M * d * V, f_ce_bwd_logits, u_ce_bwd, 3)
+    del h, W, ws, L, dH, dW
     torch.cuda.empty_cache()
     # config 5: one layer of the block backward (SwiGLU MLP + RMSNorm) at 8B-like shape
     M, d, F = 8192, 4096, 14336

@@ -52,6 +52,8 @@ _SIGS = {
     "coda_gemm_res_sumsq_bwd": (I, [P, I, P, I, P, I, P, I, P, I, P, I, I, I, I, P]),
     "coda_gemm_wgrad": (I, [P, I, P, I, P, I, I, I, I, I, P]),
     "coda_lmhead_ce_bwd": (I, [P, I, P, I, P, P, F, P, I, P, I, P, SZ, I, I, I, P]),
+    "coda_lmhead_ce_logits": (I, [P, I, P, I, P, P, P, P, P, I, P, SZ, I, I, I, P]),
+    "coda_lmhead_ce_bwd_logits": (I, [P, I, P, I, P, P, F, P, I, P, I, P, I, I, I, I, P]),
     # include/coda_unfused.h
     "coda_unfused_add": (I, [P, I, P, I, P, I, I, I, P]),
     "coda_unfused_add_rmsnorm": (I, [P, I, P, I, P, F, P, I, P, I, P, I, I, P]),
@@ -260,6 +262,25 @@ def coda_lmhead_ce(H, W, labels, lse=None, loss_row=None, loss_mean=None, ws=Non
     return lse, loss_row, loss_mean
 
 
+def coda_lmhead_ce_logits(H, W, labels, lse=None, loss_row=None, loss_mean=None, logits=None, ws=None):
+    M, d = H.shape
+    V = W.shape[1]
+    if lse is None:
+        lse = _empty((M,), torch.float32, H)
+    if loss_row is None:
+        loss_row = _empty((M,), torch.float32, H)
+    if loss_mean is None:
+        loss_mean = _empty((1,), torch.float32, H)
+    if logits is None:
+        logits = _empty((M, V), torch.bfloat16, H)
+    if ws is None:
+        ws = _empty((max(coda_lmhead_ce_workspace(M, V), 16),), torch.uint8, H)
+    _call("coda_lmhead_ce_logits", _ptr(H), _ld(H), _ptr(W), _ld(W), _ptr(labels), _ptr(lse), _ptr(loss_row),
+          _ptr(loss_mean), _ptr(logits), _ld(logits), _ptr(ws), ws.numel() * ws.element_size(), M, V, d,
+          _stream())
+    return lse, loss_row, loss_mean, logits
+
+
 # ----------------------------------------------------------------------------
 # backward
 # ----------------------------------------------------------------------------
@@ -346,6 +367,20 @@ def coda_lmhead_ce_bwd(H, W, labels, lse, grad_scale: float, dH=None, dW=None, w
         ws = _empty((max(rows * V * 2, coda_lmhead_ce_bwd_workspace(M, V, d), 16),), torch.uint8, H)
     _call("coda_lmhead_ce_bwd", _ptr(H), _ld(H), _ptr(W), _ld(W), _ptr(labels), _ptr(lse),
           ctypes.c_float(grad_scale), _ptr(dH), _ld(dH), _ptr(dW), _ld(dW), _ptr(ws), ws.numel() * ws.element_size(),
+          M, V, d, _stream())
+    return dH, dW
+
+
+def coda_lmhead_ce_bwd_logits(H, W, labels, lse, grad_scale: float, logits, dH=None, dW=None):
+    """logits (kept by coda_lmhead_ce_logits) is overwritten with the dlogits."""
+    M, d = H.shape
+    V = W.shape[1]
+    if dH is None:
+        dH = _empty((M, d), torch.bfloat16, H)
+    if dW is None:
+        dW = _empty((d, V), torch.float32, H)
+    _call("coda_lmhead_ce_bwd_logits", _ptr(H), _ld(H), _ptr(W), _ld(W), _ptr(labels), _ptr(lse),
+          ctypes.c_float(grad_scale), _ptr(logits), _ld(logits), _ptr(dH), _ld(dH), _ptr(dW), _ld(dW),
           M, V, d, _stream())
     return dH, dW
 

@@ -133,6 +133,29 @@ __global__ void __launch_bounds__(1024) ce_reduce_kernel(const float* __restrict
   }
 }
 
+// dlogits from stored bf16 logits, in place: D_ik = (exp(l_ik - lse_i) -
+// [k == label_i]) * scale, the gradient of scale * sum_i loss_i (reading
+// notes section 2, "Cross-entropy loss").  A thread takes one 16-byte chunk
+// (8 logits) of every gridDim.y-th row.
+__global__ void __launch_bounds__(256) ce_dlogits_kernel(uint16_t* __restrict__ L, int ldl,
+                                                         const int32_t* __restrict__ labels,
+                                                         const float* __restrict__ lse, float scale,
+                                                         int M, int V) {
+  const int c = blockIdx.x * 256 + (int)threadIdx.x;
+  if (8 * c >= V) return;
+  for (int i = blockIdx.y; i < M; i += gridDim.y) {
+    uint16_t* p = L + (size_t)i * ldl + 8 * c;
+    const float ls = lse[i];
+    const int y = labels[i] - 8 * c;
+    float v[8];
+    unpack8(ld16(p), v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v[e] = (__builtin_amdgcn_exp2f((v[e] - ls) * LOG2E) - (y == e ? 1.0f : 0.0f)) * scale;
+    st16(p, pack8(v));
+  }
+}
+
 // Deterministic mean of the row losses: one workgroup, fixed-order tree.
 __global__ void __launch_bounds__(1024) mean_kernel(const float* __restrict__ x, int M,
                                                     float* __restrict__ out) {
@@ -442,9 +465,11 @@ coda_status coda_gemm_swiglu(const coda_bf16* A, int lda, const coda_bf16* Wgu, 
 #undef CODA_SW
 }
 
-coda_status coda_lmhead_ce(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
-                           const int32_t* labels, float* lse, float* loss_row, float* loss_mean,
-                           void* ws, size_t ws_bytes, int M, int V, int d, hipStream_t stream) {
+static coda_status lmhead_ce_common(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
+                                    const int32_t* labels, float* lse, float* loss_row,
+                                    float* loss_mean, coda_bf16* logits, int ldl, bool keep,
+                                    void* ws, size_t ws_bytes, int M, int V, int d,
+                                    hipStream_t stream) {
   Check c;
   c.shape(M >= 0 && V >= 0 && d >= 0);
   c.bmat(H, ldh, d, true, M);
@@ -453,6 +478,7 @@ coda_status coda_lmhead_ce(const coda_bf16* H, int ldh, const coda_bf16* W, int 
   c.vec(lse, true, false, M);
   c.vec(loss_row, false);
   c.vec(loss_mean, false);
+  if (keep) c.bmat(logits, ldl, V, true, M);
   c.shape(V % 8 == 0 && d % 8 == 0);
   if (c.st != CODA_OK) return c.st;
   if (M == 0 || V == 0) return CODA_OK;
@@ -465,8 +491,13 @@ coda_status coda_lmhead_ce(const coda_bf16* H, int ldh, const coda_bf16* W, int 
   float* tgt = ps + (size_t)M * np;
   float* lrow = tgt + M;
   if (loss_row == nullptr) loss_row = lrow;
-  EpiCE e{labels, pm, ps, tgt, M};
-  if (coda_status s = launch_gemm<false, true>(W, ldw, H, ldh, V, M, d, e, stream)) return s;
+  if (keep) {
+    EpiCE<true> e{labels, pm, ps, tgt, M, logits, ldl};
+    if (coda_status s = launch_gemm<false, true>(W, ldw, H, ldh, V, M, d, e, stream)) return s;
+  } else {
+    EpiCE<false> e{labels, pm, ps, tgt, M, nullptr, 0};
+    if (coda_status s = launch_gemm<false, true>(W, ldw, H, ldh, V, M, d, e, stream)) return s;
+  }
   hipLaunchKernelGGL(ce_reduce_kernel, dim3(cdiv(M, CE_TOK)), dim3(CE_TOK * CE_SLICES), 0, stream,
                      pm, ps, tgt, labels, np, M, M, V, lse, loss_row);
   if (coda_status s = launched()) return s;
@@ -475,6 +506,21 @@ coda_status coda_lmhead_ce(const coda_bf16* H, int ldh, const coda_bf16* W, int 
     return launched();
   }
   return CODA_OK;
+}
+
+coda_status coda_lmhead_ce(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
+                           const int32_t* labels, float* lse, float* loss_row, float* loss_mean,
+                           void* ws, size_t ws_bytes, int M, int V, int d, hipStream_t stream) {
+  return lmhead_ce_common(H, ldh, W, ldw, labels, lse, loss_row, loss_mean, nullptr, 0, false, ws,
+                          ws_bytes, M, V, d, stream);
+}
+
+coda_status coda_lmhead_ce_logits(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
+                                  const int32_t* labels, float* lse, float* loss_row,
+                                  float* loss_mean, coda_bf16* logits, int ldl, void* ws,
+                                  size_t ws_bytes, int M, int V, int d, hipStream_t stream) {
+  return lmhead_ce_common(H, ldh, W, ldw, labels, lse, loss_row, loss_mean, logits, ldl, true, ws,
+                          ws_bytes, M, V, d, stream);
 }
 
 coda_status coda_gemm_swiglu_bwd(const coda_bf16* dOut, int ldd, const coda_bf16* Wd, int ldw,
@@ -663,6 +709,37 @@ coda_status coda_lmhead_ce_bwd(const coda_bf16* H, int ldh, const coda_bf16* W, 
       return s;
   }
   return CODA_OK;
+}
+
+coda_status coda_lmhead_ce_bwd_logits(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
+                                      const int32_t* labels, const float* lse, float grad_scale,
+                                      coda_bf16* logits, int ldl, coda_bf16* dH, int lddh,
+                                      float* dW, int lddw, int M, int V, int d,
+                                      hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && V >= 0 && d >= 0);
+  c.bmat(H, ldh, d, true, M);
+  c.bmat(W, ldw, V);
+  c.vec(labels, true, false, M);
+  c.vec(lse, true, false, M);
+  c.bmat(logits, ldl, V, true, M);
+  c.bmat(dH, lddh, d, true, M);
+  c.fmat(dW, lddw, V);
+  c.shape(V % 8 == 0 && d % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (V == 0 || d == 0) return CODA_OK;
+  if (coda_status st = device_ok()) return st;
+  if (M == 0)  // no rows: dW = H^T D over an empty reduction = 0
+    return coda_gemm_wgrad(H, ldh, nullptr, V, dW, lddw, 0, d, V, 0, stream);
+  // 1) dlogits in place of the logits
+  hipLaunchKernelGGL(ce_dlogits_kernel, dim3(cdiv(V / 8, 256), M < 2048 ? M : 2048), dim3(256), 0,
+                     stream, logits, ldl, labels, lse, grad_scale, M, V);
+  if (coda_status s = launched()) return s;
+  // 2) dH[M x d] = D W^T: features = d (rows of W, contiguous along V)
+  EpiLinear<false, false> e2{nullptr, nullptr, 0, dH, lddh};
+  if (coda_status s = launch_gemm<true, true>(W, ldw, logits, ldl, d, M, V, e2, stream)) return s;
+  // 3) dW[d x V] = H^T D
+  return coda_gemm_wgrad(H, ldh, logits, ldl, dW, lddw, M, d, V, 0, stream);
 }
 
 }  // extern "C"

@@ -445,18 +445,26 @@ struct EpiSwiglu {
 // ---------------------------------------------------------------------------
 // LM-head cross-entropy statistics (notes sec. 2 "Cross-entropy loss"):
 // per (token, wave feature tile) running max m and sum exp(l - m) of the fp32
-// logits, plus the gathered target logit.  Logits are never stored.
+// logits, plus the gathered target logit.  The statistics come from the fp32
+// logits; KEEP also writes the logits rounded to bf16 (through the released
+// LDS, whole rows per store), for a backward that does not recompute them.
 // ---------------------------------------------------------------------------
+template <bool KEEP>
 struct EpiCE {
   const int32_t* labels;
   float* part_m;  // [nparts x ldpart], ldpart >= M
   float* part_s;
   float* tgt;
   int ldpart;
+  uint16_t* logits;  // KEEP: bf16 [M x V], leading dimension ldl
+  int ldl;
+
+  static constexpr int LDS_BYTES = KEEP ? STAGE_LDS : 0;
 
   template <int RI, int CI>
-  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g, char* smem = nullptr) const {
     const Lane L(g);
+    [[maybe_unused]] const Stage stage(smem);
     int lab[CI];
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) lab[ci] = vload(labels, g.tw0 + L.t(ci), g.T);
@@ -473,7 +481,10 @@ struct EpiCE {
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) acc8(acc, ri, ci, h, l[ri][h]);
+        for (int h = 0; h < 2; ++h) {
+          acc8(acc, ri, ci, h, l[ri][h]);
+          if constexpr (KEEP) stage.put(g, ci, ri, h, pack8(l[ri][h]));
+        }
       // Max and sum-exp per 8-feature group; a group lies entirely inside or
       // entirely past the vocabulary (V % 8 == 0), so masking is per group.
       float m = -INFINITY;
@@ -530,6 +541,7 @@ struct EpiCE {
         part_s[(size_t)g.pf * ldpart + t] = st;
       }
     }
+    if constexpr (KEEP) stage.flush<CI>(g, TileView<2>(logits, ldl, g.tw0, g.fw0));
   }
 };
 

@@ -156,6 +156,16 @@ coda_status coda_lmhead_ce(const coda_bf16* H, int ldh, const coda_bf16* W, int 
                            const int32_t* labels, float* lse, float* loss_row, float* loss_mean,
                            void* ws, size_t ws_bytes, int M, int V, int d, hipStream_t stream);
 
+/* coda_lmhead_ce that also keeps the logits: the same statistics, taken from
+ * the fp32 logits, plus logits (bf16, M x V, leading dimension ldl, required)
+ * written by the same epilogue.  For coda_lmhead_ce_bwd_logits, which then
+ * needs no recompute GEMM; this trades the Cut-Cross-Entropy-style recompute
+ * (reading notes section 2) for 2 M V bytes of HBM. */
+coda_status coda_lmhead_ce_logits(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
+                                  const int32_t* labels, float* lse, float* loss_row,
+                                  float* loss_mean, coda_bf16* logits, int ldl, void* ws,
+                                  size_t ws_bytes, int M, int V, int d, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Backward ("reverse fusion", reading notes section 3; paper Figure 9)
  * ------------------------------------------------------------------------- */
@@ -223,6 +233,17 @@ coda_status coda_lmhead_ce_bwd(const coda_bf16* H, int ldh, const coda_bf16* W, 
                                const int32_t* labels, const float* lse, float grad_scale,
                                coda_bf16* dH, int lddh, float* dW, int lddw, void* ws,
                                size_t ws_bytes, int M, int V, int d, hipStream_t stream);
+
+/* The same backward from the logits coda_lmhead_ce_logits kept: an
+ * auxiliary kernel overwrites logits (bf16, M x V, ldl) in place with
+ *   D = (exp(l - lse_i) - [k == label_i]) grad_scale  (bf16),
+ * then dH = D W^T (bf16, M x d) and dW = H^T D (fp32, d x V, overwritten).
+ * The logits buffer holds D afterwards.  No workspace. */
+coda_status coda_lmhead_ce_bwd_logits(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
+                                      const int32_t* labels, const float* lse, float grad_scale,
+                                      coda_bf16* logits, int ldl, coda_bf16* dH, int lddh,
+                                      float* dW, int lddw, int M, int V, int d,
+                                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

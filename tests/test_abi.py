@@ -131,6 +131,14 @@ def test_fused_validation(L):
                                 128, None, 0, 16, 128, 64, None) == 6
     # col_reduce: mparts < 1
     assert L.coda_col_reduce(A16, 0, 64, A16b, None) == 2
+    # lmhead with stored logits: NULL logits, then ldl < V
+    assert L.coda_lmhead_ce_logits(A16, 64, A16b, 128, A16c, A16, None, None, None, 128, A16b,
+                                   1 << 20, 16, 128, 64, None) == 1
+    assert L.coda_lmhead_ce_logits(A16, 64, A16b, 128, A16c, A16, None, None, A16c, 64, A16b,
+                                   1 << 20, 16, 128, 64, None) == 2
+    # lmhead bwd from stored logits: NULL logits
+    assert L.coda_lmhead_ce_bwd_logits(A16, 64, A16b, 128, A16c, A16, ctypes.c_float(1.0), None,
+                                       128, A16b, 64, A16c, 128, 16, 128, 64, None) == 1
 
 
 def test_unfused_validation(L):

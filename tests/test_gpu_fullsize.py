@@ -152,6 +152,35 @@ def test_config4_fullsize():
     assert dWs <= 2e-2 * dWa
 
 
+def test_config4_fullsize_stored_logits():
+    """The stored-logits forward and backward at the full LM-head shape."""
+    c = S.CONFIGS[4]
+    M, d, V = c["M"], c["d"], c["V"]
+    say(f"case: config 4 full size, stored logits, M={M} d={d} V={V}")
+    p = S.lmhead_inputs(4, M, d, V)
+    coda = C()
+    H, W, lab = dev(p["h"]), dev(p["W"]), dev(p["labels"])
+    lse, loss_row, loss_mean, logits = coda.coda_lmhead_ce_logits(H, W, lab)
+    rows = sample(M, seed=8)
+    h64, W64 = p["h"].f64(), p["W"].f64()
+    l_rows = rows_of(logits, rows)
+    dH, dW = coda.coda_lmhead_ce_bwd_logits(H, W, lab, lse, 1.0 / M, logits)
+    torch.cuda.synchronize()
+    assert_close(l_rows, O.gemm(h64[rows], W64), "logits")
+    lse_r, loss_r, _ = O.lmhead_ce(h64[rows], W64, p["labels"][rows])
+    assert_close(rows_of(lse, rows), lse_r, "lse")
+    assert_close(rows_of(loss_row, rows), loss_r, "loss_row")
+    lr = loss_row.double().cpu().numpy()
+    assert abs(float(loss_mean.item()) - lr.mean()) <= 1e-5 * abs(lr.mean())
+    dh_r, _, D_r = O.lmhead_ce_bwd(h64[rows], W64, p["labels"][rows], 1.0 / M)
+    assert_close(rows_of(logits, rows), D_r, "dlogits")
+    assert_close(rows_of(dH, rows), dh_r, "dh")
+    dWs = dW.double().sum(1).abs().max().item()
+    dWa = dW.double().abs().max().item()
+    say(f"  max|row sum of dW| = {dWs:.3e} (max|dW| = {dWa:.3e})")
+    assert dWs <= 2e-2 * dWa
+
+
 def test_config4_full_vocab_wgrad_small_m():
     """The full 2048 x 128256 weight gradient, exactly, at M = 64 rows."""
     M, d, V = 64, 2048, 128256

@@ -281,3 +281,37 @@ def test_fuzz_lmhead_ce(seed):
     assert_close(f64(dH), dh_r, "dh")
     assert_close(dW.cpu().numpy(), dW_r, "dW")
     assert intact(Hf, dH) and intact(Wf, dW)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_fuzz_lmhead_ce_logits(seed):
+    """The stored-logits forward and its backward (dlogits in place)."""
+    rng = rng_of("lmhead_logits", seed)
+    M, _ = dims(rng)
+    d = m8(rng, 8, 520)
+    V = m8(rng, 8, 1600)
+    say(f"case: fuzz lmhead ce (stored logits) seed={seed} M={M} d={d} V={V}")
+    h = S.normal_bf16(rng.integers(1 << 30), (M, d))
+    W = S.normal_bf16(rng.integers(1 << 30), (d, V), std=d ** -0.5)
+    labels = rng.integers(0, V, M).astype(np.int32)
+    labels[: min(M, 2)] = [0, V - 1][: min(M, 2)]
+    coda = C()
+    H, Wt, lab = strided_in(h, rng), strided_in(W, rng), vec(labels)
+    Lf, logits = strided_out(M, V, torch.bfloat16, rng)
+    lse, loss_row, loss_mean, _ = coda.coda_lmhead_ce_logits(H, Wt, lab, logits=logits)
+    torch.cuda.synchronize()
+    l_gpu = f64(logits)
+    Hf, dH = strided_out(M, d, torch.bfloat16, rng)
+    Wf, dW = strided_out(d, V, torch.float32, rng)
+    coda.coda_lmhead_ce_bwd_logits(H, Wt, lab, lse, 1.0 / M, logits, dH=dH, dW=dW)
+    torch.cuda.synchronize()
+    assert_close(l_gpu, O.gemm(h.f64(), W.f64()), "logits")
+    lse_r, loss_r, mean_r = O.lmhead_ce(h.f64(), W.f64(), labels)
+    assert_close(f64(lse), lse_r, "lse")
+    assert_close(f64(loss_row), loss_r, "loss_row")
+    assert abs(float(loss_mean.item()) - mean_r) <= 1e-3 * abs(mean_r)
+    dh_r, dW_r, D_r = O.lmhead_ce_bwd(h.f64(), W.f64(), labels, 1.0 / M)
+    assert_close(f64(logits), D_r, "dlogits (in place of the logits)")
+    assert_close(f64(dH), dh_r, "dh")
+    assert_close(dW.cpu().numpy(), dW_r, "dW")
+    assert intact(Lf, logits) and intact(Hf, dH) and intact(Wf, dW)
