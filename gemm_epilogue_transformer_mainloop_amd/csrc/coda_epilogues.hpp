@@ -611,92 +611,100 @@ struct EpiSwigluBwd {
   // released (32 KiB per wave, 128 KiB per workgroup).
   static constexpr int LDS_BYTES = 4 * 32768;
 
-  // Each wave works on its 128-token x 256-column pre/dpre tile in phases of
-  // 64 tokens (32 KiB): LDS-DMA of whole 512-byte row segments into the
-  // wave's LDS slice; the pair map in the accumulator layout, reading pre and
-  // writing dpre in place; then the rows read back linearly and stored as
-  // whole row segments.  Row r keeps its 16-byte chunk c at position
-  // c ^ (r & 7), so the accumulator-layout accesses (32 rows, one chunk) hit
-  // distinct banks.  Loads and stores of global memory thereby cover whole
-  // rows, not 16-byte pieces of 32 rows.
+  // Each wave works on its (32 CI)-token x 256-column pre/dpre tile in CI
+  // phases of 32 tokens (16 KiB), double-buffered in its 32 KiB LDS slice:
+  // LDS-DMA of whole 512-byte row segments; the pair map in the accumulator
+  // layout, reading pre and writing dpre in place; then the rows read back
+  // linearly and stored as whole row segments.  Phase p+2's DMA goes into
+  // phase p's buffer once its rows are back in registers, before its stores,
+  // so each phase's data arrives while the previous phase computes and
+  // stores.  Row r keeps its 16-byte chunk c at position c ^ (r & 7), so the
+  // accumulator-layout accesses (32 rows, one chunk) hit distinct banks.
+  //
+  // Waits: LDS-DMA loads complete in issue order, stores in any order
+  // relative to them.  While a phase's DMA is incomplete every DMA issued
+  // after it is outstanding too, so "at most (DMA instructions issued
+  // after it) outstanding" implies it is complete, whatever the stores do.
   template <int RI, int CI>
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g, char* smem) const {
-    static_assert(CI % 2 == 0, "phases of two 32-token columns");
+    static_assert(CI >= 2, "at least two 32-token phases");
+    constexpr int NI = 16;  // DMA / store instructions per phase (2 rows each)
     const Lane L(g);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     char* reg = smem + wave * 32768;
     const int rlo = g.lane >> 5, pos = g.lane & 31;
     const TileView<2> po(dpre, lddp, g.tw0, 2 * g.fw0);
     const int cols = 2 * L.F;  // pre columns left from the wave tile origin
-    // Phase p's DMA is issued once phase p-1's rows are back in registers and
-    // before its stores, so the stores drain while the next rows arrive.
     auto fetch = [&](int p) {
-      const uint16_t* base = pre + (size_t)(g.tw0 + 64 * p) * ldp + 2 * g.fw0;
+      const uint16_t* base = pre + (size_t)(g.tw0 + 32 * p) * ldp + 2 * g.fw0;
+      char* buf = reg + (p & 1) * 16384;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
+      for (int i = 0; i < NI; ++i) {
         const int r = 2 * i + rlo, c = pos ^ (r & 7);
-        const bool ok = 64 * p + r < L.T && 8 * c < cols;
-        dma16(base, 0x7fffffffu, ok ? (uint32_t)(r * ldp + 8 * c) * 2u : OOB, reg + i * 1024);
+        const bool ok = 32 * p + r < L.T && 8 * c < cols;
+        dma16(base, 0x7fffffffu, ok ? (uint32_t)(r * ldp + 8 * c) * 2u : OOB, buf + i * 1024);
       }
     };
     fetch(0);
+    fetch(1);
 #pragma unroll
-    for (int p = 0; p < CI / 2; ++p) {
-      wait_vmcnt<0>();
+    for (int p = 0; p < CI; ++p) {
+      if (p + 1 < CI)
+        wait_vmcnt<NI>();  // phase p+1's DMA is the only later one
+      else
+        wait_vmcnt<0>();
+      char* buf = reg + (p & 1) * 16384;
       // dpre from pre and da in the accumulator layout, in place.
+      const int ci = p;
+      const int r = g.lt;
+      float ss = 0.0f;
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int ci = 2 * p + cc;
-        const int r = 32 * cc + g.lt;
-        float ss = 0.0f;
+      for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
-        for (int ri = 0; ri < RI; ++ri)
+        for (int h = 0; h < 2; ++h) {
+          const bool ok = L.ok(ci, ri, h);
+          float dav[8];
+          acc8(acc, ri, ci, h, dav);
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const bool ok = L.ok(ci, ri, h);
-            float dav[8];
-            acc8(acc, ri, ci, h, dav);
+          for (int c = 0; c < 2; ++c) {  // two 16-byte chunks = 4 pairs each
+            const int chunk = 8 * ri + 4 * h + 2 * g.hh + c;
+            char* a = buf + r * 512 + ((chunk ^ (r & 7)) << 4);
+            float pvv[8], out[8];
+            unpack8(ld16(a), pvv);
+            float part = 0.0f;
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {  // two 16-byte chunks = 4 pairs each
-              const int chunk = 8 * ri + 4 * h + 2 * g.hh + c;
-              char* a = reg + r * 512 + ((chunk ^ (r & 7)) << 4);
-              float pvv[8], out[8];
-              unpack8(ld16(a), pvv);
-              float part = 0.0f;
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const float da = dav[4 * c + q];
-                const float gg = pvv[2 * q], uu = pvv[2 * q + 1];
-                const float sg = sigmoidf_(gg);
-                const float dg = da * uu * sg * (1.0f + gg * (1.0f - sg));
-                const float du = da * gg * sg;
-                out[2 * q] = dg;
-                out[2 * q + 1] = du;
-                part += dg * gg + du * uu;
-              }
-              ss += ok ? part : 0.0f;
-              st16(a, pack8(out));
+            for (int q = 0; q < 4; ++q) {
+              const float da = dav[4 * c + q];
+              const float gg = pvv[2 * q], uu = pvv[2 * q + 1];
+              const float sg = sigmoidf_(gg);
+              const float dg = da * uu * sg * (1.0f + gg * (1.0f - sg));
+              const float du = da * gg * sg;
+              out[2 * q] = dg;
+              out[2 * q + 1] = du;
+              part += dg * gg + du * uu;
             }
+            ss += ok ? part : 0.0f;
+            st16(a, pack8(out));
           }
-        if constexpr (HAS_SPART) {
-          ss = sum_halves(ss);
-          const bool w = g.hh == 0 && L.tok(ci) && L.F > 0;
-          const int t = g.tw0 + L.t(ci);
-          if (w) spart[(size_t)t * nparts + g.pf] = ss;
         }
+      if constexpr (HAS_SPART) {
+        ss = sum_halves(ss);
+        const bool w = g.hh == 0 && L.tok(ci) && L.F > 0;
+        const int t = g.tw0 + L.t(ci);
+        if (w) spart[(size_t)t * nparts + g.pf] = ss;
       }
       // Whole rows back out: instruction i stores rows 2i and 2i + 1.
-      u32x4 sv[32];
+      u32x4 sv[NI];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) sv[i] = ld16(reg + i * 1024 + 16 * g.lane);
-      if (p + 1 < CI / 2) {
-        wait_lgkmcnt0();  // the slice is read before the next DMA refills it
-        fetch(p + 1);
+      for (int i = 0; i < NI; ++i) sv[i] = ld16(buf + i * 1024 + 16 * g.lane);
+      if (p + 2 < CI) {
+        wait_lgkmcnt0();  // the buffer is read before the next DMA refills it
+        fetch(p + 2);
       }
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int r = 2 * i + rlo, c = pos ^ (r & 7);
-        po.store16(64 * p + r, 8 * c, 64 * p + r < L.T && 8 * c < cols, sv[i]);
+      for (int i = 0; i < NI; ++i) {
+        const int rr = 2 * i + rlo, c = pos ^ (rr & 7);
+        po.store16(32 * p + rr, 8 * c, 32 * p + rr < L.T && 8 * c < cols, sv[i]);
       }
     }
   }
