@@ -201,8 +201,9 @@ def cold_cache(torch, coda, synth, p, T, dims, n_rope, total_flops, min_bytes=60
             "bytes_rotated": int(nsets * per_set), "steps": steps}
 
 
-def cpu_baseline(p, dims, n_rope, min_seconds=10.0, max_steps=20):
-    """The fp64 oracle timed on the host on whole config-2 steps (at least min_seconds)."""
+def cpu_baseline(p, dims, n_rope, min_seconds=12.0, max_steps=60):
+    """The fp64 oracle timed on the host on whole config-2 steps (at least
+    min_seconds, at most max_steps: about 12-30 s of host work)."""
     from oracle import coda_oracle as O
     from threadpoolctl import threadpool_info
 
@@ -701,6 +702,10 @@ def main():
         if k in flops:
             tf = flops[k] / (v * 1e-3) / 1e12
             ent.update(tflops=round(tf, 1), pct_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2))
+        if k == "row_rms":  # aux reduction: algorithmic bytes (partials in, r out) per time
+            nb = M * coda.coda_nparts(d) * 4 + M * 4
+            ent.update(bytes=nb, gbs=round(nb / (v * 1e-3) / 1e9, 1),
+                       pct_hbm=round(100 * nb / (v * 1e-3) / 1e9 / PEAK_HBM_GBS, 2))
         ops[k] = ent
     log("per-op (HIP events on the launch stream):")
     for k, v in ops.items():
