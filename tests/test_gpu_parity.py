@@ -279,10 +279,11 @@ def test_lmhead_bad_label_is_nan():
     labels[3] = V
     labels[5] = -1
     lse, loss_row, _ = C().coda_lmhead_ce(dev(p["h"]), dev(p["W"]), dev(labels))
+    _, loss_row2, _, _ = C().coda_lmhead_ce_logits(dev(p["h"]), dev(p["W"]), dev(labels))
     torch.cuda.synchronize()
-    lr = loss_row.cpu().numpy()
-    assert np.isnan(lr[3]) and np.isnan(lr[5])
-    assert np.all(np.isfinite(np.delete(lr, [3, 5])))
+    for lr in (loss_row.cpu().numpy(), loss_row2.cpu().numpy()):
+        assert np.isnan(lr[3]) and np.isnan(lr[5])
+        assert np.all(np.isfinite(np.delete(lr, [3, 5])))
 
 
 # ---------------------------------------------------------------------------
@@ -421,3 +422,12 @@ def test_empty_inputs():
                               dW=torch.full((64, 128), 5.0, device="cuda"))
     torch.cuda.synchronize()
     assert torch.all(dW == 0)
+    # LM head with no rows: the stored-logits pair; the backward writes dW = 0
+    H0 = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    W0 = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    lab0 = torch.empty((0,), dtype=torch.int32, device="cuda")
+    lse0, _, _, L0 = coda.coda_lmhead_ce_logits(H0, W0, lab0)
+    dH0, dW0 = coda.coda_lmhead_ce_bwd_logits(H0, W0, lab0, lse0, 1.0, L0,
+                                              dW=torch.full((64, 256), 5.0, device="cuda"))
+    torch.cuda.synchronize()
+    assert L0.shape == (0, 256) and dH0.shape == (0, 64) and torch.all(dW0 == 0)
