@@ -621,10 +621,13 @@ struct EpiSwigluBwd {
   // stores.  Row r keeps its 16-byte chunk c at position c ^ (r & 7), so the
   // accumulator-layout accesses (32 rows, one chunk) hit distinct banks.
   //
-  // Waits: LDS-DMA loads complete in issue order, stores in any order
-  // relative to them.  While a phase's DMA is incomplete every DMA issued
-  // after it is outstanding too, so "at most (DMA instructions issued
-  // after it) outstanding" implies it is complete, whatever the stores do.
+  // Waits: vmcnt retires vector memory operations, loads and stores alike,
+  // in issue order (the compiler's own waits on gfx950 rely on it: a load
+  // followed by two stores is awaited with vmcnt(2)).  A phase's DMA is
+  // complete once at most the operations issued after it are outstanding:
+  // the next phase's DMA and the previous phases' row stores, which stay in
+  // flight.  (The s-partial store, when there is one, only makes the wait
+  // stricter.)
   template <int RI, int CI>
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g, char* smem) const {
     static_assert(CI >= 2, "at least two 32-token phases");
@@ -649,10 +652,14 @@ struct EpiSwigluBwd {
     fetch(1);
 #pragma unroll
     for (int p = 0; p < CI; ++p) {
-      if (p + 1 < CI)
-        wait_vmcnt<NI>();  // phase p+1's DMA is the only later one
-      else
-        wait_vmcnt<0>();
+      // Operations issued after phase p's DMA: p = 0: phase 1's DMA;
+      // p = 1: phase 2's DMA (if any) and phase 0's stores; p >= 2 (its DMA
+      // went out in phase p-2, before that phase's stores): phase p-2's and
+      // p-1's stores and phase p+1's DMA (if any).
+      const int later = p == 0 ? (CI > 1 ? NI : 0)
+                      : p == 1 ? (CI > 2 ? NI : 0) + NI
+                               : 2 * NI + (p + 1 < CI ? NI : 0);
+      wait_vmcnt_le(later);
       char* buf = reg + (p & 1) * 16384;
       // dpre from pre and da in the accumulator layout, in place.
       const int ci = p;

@@ -131,6 +131,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// wait_vmcnt<n> for an n known after unrolling (0, 16, 32 or 48; anything
+// else waits for everything, which is always safe).
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  switch (n) {
+    case 16: wait_vmcnt<16>(); break;
+    case 32: wait_vmcnt<32>(); break;
+    case 48: wait_vmcnt<48>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // One operand tile: ROWS rows (features or tokens) x BK = 64 k, in one LDS
 // stage of REGION bytes.  Thread (wave w, lane l) issues NCH DMA instructions
