@@ -53,6 +53,11 @@ struct TileView {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off(t, f, ok), 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // Non-temporal store (output streamed once, not re-read by this kernel).
+  __device__ __forceinline__ void store16_nt(int t, int f, bool ok, u32x4 v) const {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off(t, f, ok), 0, 2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   __device__ __forceinline__ void store8(int t, int f, bool ok, u32x2 v) const {
     __builtin_amdgcn_raw_buffer_store_b64(v, rs, off(t, f, ok), 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -645,7 +650,7 @@ struct EpiSwigluBwd {
       for (int i = 0; i < NI; ++i) {
         const int r = 2 * i + rlo, c = pos ^ (r & 7);
         const bool ok = 32 * p + r < L.T && 8 * c < cols;
-        dma16(base, 0x7fffffffu, ok ? (uint32_t)(r * ldp + 8 * c) * 2u : OOB, buf + i * 1024);
+        dma16<true>(base, 0x7fffffffu, ok ? (uint32_t)(r * ldp + 8 * c) * 2u : OOB, buf + i * 1024);
       }
     };
     fetch(0);
@@ -711,7 +716,7 @@ struct EpiSwigluBwd {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int rr = 2 * i + rlo, c = pos ^ (rr & 7);
-        po.store16(32 * p + rr, 8 * c, 32 * p + rr < L.T && 8 * c < cols, sv[i]);
+        po.store16_nt(32 * p + rr, 8 * c, 32 * p + rr < L.T && 8 * c < cols, sv[i]);
       }
     }
   }

@@ -100,6 +100,9 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // (wait_vmcnt) before the barrier that publishes the stage.  vmcnt counts in
 // issue order, so waits the compiler inserts for its own later loads stay
 // correct (they may only wait longer).
+// NT marks the load non-temporal (data read once, e.g. an epilogue's input
+// tile), so it does not displace the GEMM operands in the caches.
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const void* base, uint32_t range, uint32_t voff, char* dst) {
   typedef __attribute__((ext_vector_type(4))) int i32x4;
   const uint64_t b = reinterpret_cast<uint64_t>(base);
@@ -111,13 +114,22 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t range, uint32_t
   const int m0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_ptr_t)dst);
   // A SALU write of M0 needs one wait state before an LDS-DMA instruction
   // reads it; s_nop 1 gives two.
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 1\n\t"
-      "buffer_load_dwordx4 %0, %1, 0 offen lds"
-      :
-      : "v"(voff), "s"(rs), "s"(m0)
-      : "memory", "m0");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 1\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen nt lds"
+        :
+        : "v"(voff), "s"(rs), "s"(m0)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 1\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        :
+        : "v"(voff), "s"(rs), "s"(m0)
+        : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N), other counters unconstrained (gfx9 encoding: vmcnt in
