@@ -111,7 +111,9 @@ struct Stage {
     const int r = ci * 32 + g.lt, c = 4 * ri + 2 * h + g.hh;
     st16(reg + r * 256 + ((c ^ (r & 15)) << 4), v);
   }
-  template <int CI>
+  // NT: non-temporal stores, for large outputs that this kernel streams
+  // out once and that would otherwise displace the GEMM operands.
+  template <int CI, bool NT = false>
   __device__ __forceinline__ void flush(const Geom& g, const TileView<2>& out) const {
     const int T = g.T - g.tw0, F = g.F - g.fw0;
     const int rlo = g.lane >> 4, pos = g.lane & 15;
@@ -123,7 +125,10 @@ struct Stage {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = 4 * (i0 + i) + rlo, c = pos ^ (r & 15);
-        out.store16(r, 8 * c, r < T && 8 * c < F, sv[i]);
+        if constexpr (NT)
+          out.store16_nt(r, 8 * c, r < T && 8 * c < F, sv[i]);
+        else
+          out.store16(r, 8 * c, r < T && 8 * c < F, sv[i]);
       }
     }
   }
@@ -443,7 +448,7 @@ struct EpiSwiglu {
         ao.store8(L.t(ci), ri * 16 + g.hh * 8, half, (u32x2){out[0], out[1]});
       }
     }
-    if constexpr (HAS_PRE) Stage(smem).flush<CI>(g, po);
+    if constexpr (HAS_PRE) Stage(smem).flush<CI, true>(g, po);
   }
 };
 
@@ -546,7 +551,7 @@ struct EpiCE {
         part_s[(size_t)g.pf * ldpart + t] = st;
       }
     }
-    if constexpr (KEEP) stage.flush<CI>(g, TileView<2>(logits, ldl, g.tw0, g.fw0));
+    if constexpr (KEEP) stage.flush<CI, true>(g, TileView<2>(logits, ldl, g.tw0, g.fw0));
   }
 };
 
@@ -594,7 +599,7 @@ struct EpiCEBwd {
           stage.put(g, ci, ri, h, pack8(v));
         }
     }
-    stage.flush<CI>(g, d);
+    stage.flush<CI, true>(g, d);
   }
 };
 
