@@ -854,7 +854,8 @@ struct EpiF32 {
   int ld;
 
   // The plain store goes through the released LDS (fp32 rows of 512 bytes,
-  // 64 rows per 32 KiB wave slice, so two passes of two 32-token columns);
+  // 64 rows per 32 KiB wave slice, so two passes of two 32-token columns)
+  // and is non-temporal (weight gradients are written once, 0.1-1 GB);
   // the accumulating form keeps its register path.
   static constexpr int LDS_BYTES = ACCUM ? 0 : STAGE_LDS;
 
@@ -891,7 +892,7 @@ struct EpiF32 {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int r = 2 * (i0 + i) + rlo, c = pos ^ (r & 7);
-            o.store16(64 * p + r, 4 * c, 64 * p + r < L.T && 4 * c < L.F, sv[i]);
+            o.store16_nt(64 * p + r, 4 * c, 64 * p + r < L.T && 4 * c < L.F, sv[i]);
           }
         }
       }
