@@ -393,6 +393,40 @@ struct EpiRope {
 // a_j = g sigmoid(g) v; optional Pre = bf16(g, v) for the backward pass.
 // The GEMM's feature space is the interleaved 2F columns.
 // ---------------------------------------------------------------------------
+// The SwiGLU output tile (CI x 32 tokens x 64 act columns, 128-byte rows)
+// staged the same way through the wave's LDS slice: chunk c (8 columns) of
+// row r sits at position c ^ (r & 7); flush() stores eight whole rows per
+// instruction, non-temporal.  Fa = act columns left from the wave tile
+// origin (a multiple of 4: the last chunk may hold only 4 valid columns).
+struct StageAct {
+  char* reg;
+  __device__ __forceinline__ explicit StageAct(char* smem)
+      : reg(smem + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * 32768) {}
+  __device__ __forceinline__ void put(const Geom& g, int ci, int ri, u32x4 v) const {
+    const int r = ci * 32 + g.lt, c = 2 * ri + g.hh;
+    st16(reg + r * 128 + ((c ^ (r & 7)) << 4), v);
+  }
+  template <int CI>
+  __device__ __forceinline__ void flush(const Geom& g, const TileView<2>& out, int Fa) const {
+    const int T = g.T - g.tw0;
+    const int rlo = g.lane >> 3, pos = g.lane & 7;
+#pragma unroll
+    for (int i0 = 0; i0 < CI * 4; i0 += 8) {
+      u32x4 sv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sv[i] = ld16(reg + (i0 + i) * 1024 + 16 * g.lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * (i0 + i) + rlo, c = pos ^ (r & 7);
+        const bool full = r < T && 8 * c + 8 <= Fa;
+        const bool half = r < T && 8 * c + 4 <= Fa && !full;
+        out.store16_nt(r, 8 * c, full, sv[i]);
+        out.store8(r, 8 * c, half, (u32x2){sv[i][0], sv[i][1]});
+      }
+    }
+  }
+};
+
 template <bool HAS_R, bool HAS_PRE>
 struct EpiSwiglu {
   const float* r;
@@ -401,16 +435,19 @@ struct EpiSwiglu {
   uint16_t* pre;
   int ldp;
 
-  static constexpr int LDS_BYTES = HAS_PRE ? STAGE_LDS : 0;
+  // pre (when kept) and then act leave through the released LDS.
+  static constexpr int LDS_BYTES = STAGE_LDS;
 
   template <int RI, int CI>
-  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g, char* smem = nullptr) const {
+  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g, char* smem) const {
     const Lane L(g);
     const TileView<2> ao(act, ldact, g.tw0, g.fw0 >> 1);
     const TileView<2> po(pre, ldp, g.tw0, g.fw0);
+    const StageAct sa(smem);
     float rsv[CI];
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) rsv[ci] = HAS_R ? vload(r, g.tw0 + L.t(ci), g.T) : 1.0f;
+    u32x4 aout[CI][RI];
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
       const float rs = rsv[ci];
@@ -434,21 +471,25 @@ struct EpiSwiglu {
           if constexpr (HAS_PRE) Stage(smem).put(g, ci, ri, h, pack8(v));
         }
         // Exchange with lane l ^ 32 so that each lane holds 8 consecutive
-        // a-columns (16 ri + 8 hh + 0..7) and writes them with one 16-byte store.
+        // a-columns (16 ri + 8 hh + 0..7).
         const u32x2 give = g.hh ? ah[0] : ah[1];
         const u32x2 got = {(uint32_t)__shfl_xor((int)give[0], 32), (uint32_t)__shfl_xor((int)give[1], 32)};
-        const u32x4 out = g.hh ? (u32x4){got[0], got[1], ah[1][0], ah[1][1]}
-                               : (u32x4){ah[0][0], ah[0][1], got[0], got[1]};
-        // The 16 features behind this store are all valid, or (F % 8 == 4 at
-        // the right edge) only the first 8: then the low 8 bytes are stored.
-        const int fb = ri * 32 + g.hh * 16;
-        const bool full = L.tok(ci) && fb + 16 <= L.F;
-        const bool half = L.tok(ci) && fb + 8 <= L.F && !full;
-        ao.store16(L.t(ci), ri * 16 + g.hh * 8, full, out);
-        ao.store8(L.t(ci), ri * 16 + g.hh * 8, half, (u32x2){out[0], out[1]});
+        aout[ci][ri] = g.hh ? (u32x4){got[0], got[1], ah[1][0], ah[1][1]}
+                            : (u32x4){ah[0][0], ah[0][1], got[0], got[1]};
+        if constexpr (!HAS_PRE) sa.put(g, ci, ri, aout[ci][ri]);
       }
     }
-    if constexpr (HAS_PRE) Stage(smem).flush<CI, true>(g, po);
+    if constexpr (HAS_PRE) {
+      // The slice is free again once flush() has its rows back in registers
+      // (its stores consume them; the LDS serves one wave's accesses in
+      // order); then act takes it.
+      Stage(smem).flush<CI, true>(g, po);
+#pragma unroll
+      for (int ci = 0; ci < CI; ++ci)
+#pragma unroll
+        for (int ri = 0; ri < RI; ++ri) sa.put(g, ci, ri, aout[ci][ri]);
+    }
+    sa.flush<CI>(g, ao, L.F >> 1);
   }
 };
 
