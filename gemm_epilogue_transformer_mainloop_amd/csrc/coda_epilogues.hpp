@@ -186,7 +186,7 @@ struct EpiLinear {
           stage.put(g, ci, ri, h, pack8(v));
         }
     }
-    stage.flush<CI>(g, y);
+    stage.flush<CI, HAS_RES>(g, y);  // residual-stream outputs: non-temporal
   }
 };
 
