@@ -388,11 +388,6 @@ struct EpiRope {
   }
 };
 
-// ---------------------------------------------------------------------------
-// SwiGLU pair map 2 -> 1 (paper Fig. 7): (g, v) = r * (acc_2j, acc_2j+1),
-// a_j = g sigmoid(g) v; optional Pre = bf16(g, v) for the backward pass.
-// The GEMM's feature space is the interleaved 2F columns.
-// ---------------------------------------------------------------------------
 // The SwiGLU output tile (CI x 32 tokens x 64 act columns, 128-byte rows)
 // staged the same way through the wave's LDS slice: chunk c (8 columns) of
 // row r sits at position c ^ (r & 7); flush() stores eight whole rows per
@@ -427,6 +422,11 @@ struct StageAct {
   }
 };
 
+// ---------------------------------------------------------------------------
+// SwiGLU pair map 2 -> 1 (paper Fig. 7): (g, v) = r * (acc_2j, acc_2j+1),
+// a_j = g sigmoid(g) v; optional Pre = bf16(g, v) for the backward pass.
+// The GEMM's feature space is the interleaved 2F columns.
+// ---------------------------------------------------------------------------
 template <bool HAS_R, bool HAS_PRE>
 struct EpiSwiglu {
   const float* r;
