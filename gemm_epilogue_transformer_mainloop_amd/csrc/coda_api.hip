@@ -248,7 +248,8 @@ coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, 
   const int nb = p.nTF * p.nTT;
   if (nb == 0) return CODA_OK;
   if constexpr (BT == 256 && XK && AnyWaveWidth<Epi>::value) {
-    const int split = coda_tile_split(F, T, device_cus());
+    const int cus = device_cus();
+    const int split = coda_tile_split(F, T, cus);
     if (split > 0) {
       Problem big = p, half = p;
       big.nTF = split;
@@ -257,6 +258,17 @@ coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, 
       half.nTT = cdiv(T, 128);
       hipLaunchKernelGGL((gemm_epi_kernel_split<WK, XK, Epi>), dim3(big.nTF * big.nTT + half.nTF * half.nTT),
                          dim3(NT), 0, stream, big, half, epi);
+      return launched();
+    }
+    // Under half a round of big tiles: 256 x 128 tiles run on twice as many
+    // CUs in the same single round, so each CU's k-loop and epilogue (the
+    // whole cost of a small GEMM) are about half as long.
+    if (cus > 0 && 2 * nb <= cus && cdiv(T, 128) > p.nTT) {
+      Problem none = p, half = p;
+      none.nTF = 0;
+      half.nTT = cdiv(T, 128);
+      hipLaunchKernelGGL((gemm_epi_kernel_split<WK, XK, Epi>), dim3(half.nTF * half.nTT), dim3(NT), 0,
+                         stream, none, half, epi);
       return launched();
     }
   }

@@ -71,7 +71,9 @@ int coda_mparts(int M);
  * 256 features x 256 tokens, one per compute unit at a time; when that
  * leaves the last round of tiles mostly empty, the features from
  * 256 * split on are computed in 256 x 128 tiles by the same dispatch.
- * Returns split (0: all tiles 256 x 256).  Applies to coda_gemm, the forward
+ * Returns split (0: no such split).  A problem of at most cus/2 tiles of
+ * 256 x 256 (under half a round) instead runs entirely in 256 x 128 tiles,
+ * on twice as many compute units.  Both apply to coda_gemm, the forward
  * calls, coda_gemm_swiglu_bwd, coda_gemm_res_sumsq_bwd (dX) and the GEMMs
  * of the LM head; coda_gemm_rowscale_bwd and the weight gradients always use
  * 256 x 256 tiles.  Host-only: touches no device. */
