@@ -2,9 +2,10 @@
 
     python -m gemm_epilogue_transformer_mainloop_amd.build
 
-The library is rebuilt on every call.  Packed-fp32 VALU instructions are
-disabled for the device code; the host pass warns that it does not know the
-feature, which is harmless.
+The library is rebuilt on every call: each translation unit is compiled to an
+object in parallel (one hipcc per source), then the objects are linked.
+Packed-fp32 VALU instructions are disabled for the device code; the host pass
+warns that it does not know the feature, which is harmless.
 
 The compiler's per-kernel resource report (VGPRs, AGPRs, scratch bytes per
 lane) is written to libcoda.resources.json beside the library, and the build
@@ -20,6 +21,7 @@ import os
 import re
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -28,14 +30,14 @@ LIB = os.path.join(HERE, "libcoda.so")
 RESOURCES = os.path.join(HERE, "libcoda.resources.json")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["coda_api.hip", "coda_unfused.hip"]
+SOURCES = ["coda_aux.hip", "coda_fwd.hip", "coda_pair.hip", "coda_bwd.hip", "coda_ce.hip", "coda_unfused.hip"]
+OBJDIR = os.path.join(HERE, "_build")
 
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -62,21 +64,28 @@ def parse_resources(text: str) -> dict:
     return out
 
 
-def build(verbose: bool = False, occ2: bool = False, out: str = None) -> str:
-    """Build the library.  occ2=True builds the variant whose forward and
-    data-gradient calls use two workgroups per CU (coda_mainloop_occ2.hpp)
-    into `out` (default libcoda_occ2.so); the default library does not use it."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    lib = out or (os.path.join(HERE, "libcoda_occ2.so") if occ2 else LIB)
-    tmp = lib + ".tmp"
-    cmd = [HIPCC] + FLAGS + (["-DCODA_OCC2=1"] if occ2 else []) + srcs + ["-o", tmp]
+def _compile(src: str, obj: str, extra: list, verbose: bool) -> str:
+    cmd = [HIPCC] + FLAGS + extra + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed ({res.returncode})")
-    text = res.stdout + res.stderr
+        raise RuntimeError(f"hipcc failed on {os.path.basename(src)} ({res.returncode})")
+    return res.stdout + res.stderr
+
+
+def build(verbose: bool = False, out: str = None, extra: list = None, jobs: int = None) -> str:
+    """Build the library (default: libcoda.so beside this file) and return its path."""
+    extra = list(extra or [])
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    lib = out or LIB
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs = [os.path.join(OBJDIR, os.path.basename(s).replace(".hip", ".o")) for s in srcs]
+    jobs = jobs or min(len(srcs), max(1, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        texts = list(ex.map(lambda a: _compile(a[0], a[1], extra, verbose), zip(srcs, objs)))
+    text = "\n".join(texts)
     errs = [l for l in text.splitlines()
             if "error" in l.lower() and "packed-fp32-ops" not in l]
     if errs:
@@ -84,9 +93,16 @@ def build(verbose: bool = False, occ2: bool = False, out: str = None) -> str:
     resources = parse_resources(text)
     spills = {k: v["scratch"] for k, v in resources.items() if v.get("scratch", 0) > 0}
     if spills:
-        os.remove(tmp)
         raise RuntimeError(f"kernels use scratch memory (register spills): {spills}")
-    if not occ2:
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"link failed ({res.returncode})")
+    if out is None:
         with open(RESOURCES, "w") as f:
             json.dump(resources, f, indent=1, sort_keys=True)
     os.replace(tmp, lib)
@@ -94,4 +110,4 @@ def build(verbose: bool = False, occ2: bool = False, out: str = None) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True, occ2="--occ2" in sys.argv[1:]))
+    print(build(verbose=True))

@@ -1,0 +1,141 @@
+// coda_bwd.hip - the backward ("reverse fusion") GEMM-epilogue calls: the
+// SwiGLU backward pair map with the s partials, the RMSNorm backward with the
+// delayed statistic, the data gradient with residual and the weight gradient.
+//
+// Every entry point validates its arguments before any HIP call, launches on
+// the caller's stream and returns; nothing is allocated or synchronised.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/coda.h"
+#include "coda_launch.hpp"
+
+using namespace coda;
+using namespace coda_host;
+using namespace coda_launch;
+
+extern "C" {
+
+coda_status coda_gemm_swiglu_bwd(const coda_bf16* dOut, int ldd, const coda_bf16* Wd, int ldw,
+                                 const coda_bf16* Pre, int ldp, coda_bf16* dPre, int lddp,
+                                 float* spart, int M, int F, int N, hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && F >= 0 && N >= 0 && F <= (1 << 29));
+  if (c.st != CODA_OK) return c.st;
+  c.bmat(dOut, ldd, N, true, M);
+  c.bmat(Wd, ldw, N);
+  c.bmat(Pre, ldp, 2 * F, true, M);
+  c.bmat(dPre, lddp, 2 * F, true, M);
+  c.vec(spart, false, false, M);
+  c.shape(F % 8 == 0 && N % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (M == 0 || F == 0) return CODA_OK;
+  if (coda_status s = device_ok()) return s;
+  const int np = coda_nparts(F);
+  // da[M x F] = dOut[M x N] Wd^T: features = F (rows of Wd, K-major), tokens = M.
+  if (spart) {
+    EpiSwigluBwd<true> e{Pre, ldp, dPre, lddp, spart, np};
+    return launch_gemm<true, true>(Wd, ldw, dOut, ldd, F, M, N, e, stream);
+  }
+  EpiSwigluBwd<false> e{Pre, ldp, dPre, lddp, nullptr, np};
+  return launch_gemm<true, true>(Wd, ldw, dOut, ldd, F, M, N, e, stream);
+}
+
+coda_status coda_gemm_rowscale_bwd(const coda_bf16* dY, int ldd, const coda_bf16* W1, int ldw,
+                                   const coda_bf16* U, int ldu, const coda_bf16* gamma,
+                                   const float* r, const float* s, const coda_bf16* dRes, int ldr,
+                                   coda_bf16* dU, int lddu, coda_bf16* N2, int ldn, float* gpart,
+                                   int M, int d, int N, hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && d >= 0 && N >= 0);
+  c.bmat(dY, ldd, N, true, M);
+  c.bmat(W1, ldw, N);
+  c.bmat(U, ldu, d, true, M);
+  c.vec(gamma, true, true);
+  c.vec(r, true, false, M);
+  c.vec(s, true, false, M);
+  c.bmat(dRes, ldr, d, false, M);
+  c.bmat(dU, lddu, d, true, M);
+  c.bmat(N2, ldn, d, false, M);
+  c.vec(gpart, false);
+  c.shape(d % 8 == 0 && N % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (M == 0 || d == 0) return CODA_OK;
+  if (coda_status st = device_ok()) return st;
+#define CODA_RB(HR, HN, HG)                                                             \
+  {                                                                                     \
+    EpiRowscaleBwd<HR, HN, HG> e{U, ldu, gamma, r, s, dRes, ldr, dU, lddu, N2, ldn,     \
+                                 gpart, d};                                             \
+    return launch_gemm<true, true, 256>(W1, ldw, dY, ldd, d, M, N, e, stream);          \
+  }
+  const bool hr = dRes != nullptr, hn = N2 != nullptr, hg = gpart != nullptr;
+  if (hr && hn && hg) CODA_RB(true, true, true)
+  if (hr && hn && !hg) CODA_RB(true, true, false)
+  if (hr && !hn && hg) CODA_RB(true, false, true)
+  if (hr && !hn && !hg) CODA_RB(true, false, false)
+  if (!hr && hn && hg) CODA_RB(false, true, true)
+  if (!hr && hn && !hg) CODA_RB(false, true, false)
+  if (!hr && !hn && hg) CODA_RB(false, false, true)
+  CODA_RB(false, false, false)
+#undef CODA_RB
+}
+
+coda_status coda_gemm_wgrad(const coda_bf16* X, int ldx, const coda_bf16* dY, int ldd, float* dW,
+                            int lddw, int M, int K, int N, int accumulate, hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && K >= 0 && N >= 0);
+  c.bmat(X, ldx, K, true, M);
+  c.bmat(dY, ldd, N, true, M);
+  c.fmat(dW, lddw, N);
+  c.shape(K % 8 == 0 && N % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (K == 0 || N == 0) return CODA_OK;
+  if (coda_status st = device_ok()) return st;
+  // dW[K x N] = X^T dY: features = N (dY, contiguous along N -> MN-major),
+  // tokens = K (X, contiguous along K -> MN-major), reduction = M.
+  if (accumulate) {
+    EpiF32<true> e{dW, lddw};
+    return launch_gemm<false, false>(dY, ldd, X, ldx, N, K, M, e, stream);
+  }
+  EpiF32<false> e{dW, lddw};
+  return launch_gemm<false, false>(dY, ldd, X, ldx, N, K, M, e, stream);
+}
+
+coda_status coda_gemm_res_sumsq_bwd(const coda_bf16* dU, int ldu, const coda_bf16* W, int ldw,
+                                    const coda_bf16* X, int ldx, const coda_bf16* dRes, int ldr,
+                                    coda_bf16* dX, int lddx, float* dW, int lddw, int M, int N,
+                                    int K, hipStream_t stream) {
+  Check c;
+  c.shape(M >= 0 && N >= 0 && K >= 0);
+  c.bmat(dU, ldu, N, true, M);
+  c.bmat(W, ldw, N);
+  c.bmat(dRes, ldr, K, false, M);
+  c.bmat(dX, lddx, K, true, M);
+  if (dW) {
+    c.bmat(X, ldx, K, true, M);
+    c.fmat(dW, lddw, N);
+  }
+  c.shape(N % 8 == 0 && K % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (M == 0 && dW == nullptr) return CODA_OK;
+  if (coda_status st = device_ok()) return st;
+  if (M > 0 && K > 0) {
+    // dX[M x K] = dU[M x N] W^T: features = K (rows of W, K-major over N).
+    coda_status s2;
+    if (dRes) {
+      EpiLinear<false, true> e{nullptr, dRes, ldr, dX, lddx};
+      s2 = launch_gemm<true, true>(W, ldw, dU, ldu, K, M, N, e, stream);
+    } else {
+      EpiLinear<false, false> e{nullptr, nullptr, 0, dX, lddx};
+      s2 = launch_gemm<true, true>(W, ldw, dU, ldu, K, M, N, e, stream);
+    }
+    if (s2 != CODA_OK) return s2;
+  }
+  if (dW) return coda_gemm_wgrad(X, ldx, dU, ldu, dW, lddw, M, K, N, 0, stream);
+  return CODA_OK;
+}
+
+}  // extern "C"

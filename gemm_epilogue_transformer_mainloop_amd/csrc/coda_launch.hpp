@@ -1,0 +1,94 @@
+// coda_launch.hpp - host-side launch of one fused GEMM (tile plan, grid
+// shape and kernel choice), shared by the translation units of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "../../include/coda.h"
+#include "coda_epilogues.hpp"
+#include "coda_host.hpp"
+
+namespace coda_launch {
+
+using namespace coda;
+using namespace coda_host;
+
+// Epilogues that work on any wave-tile width (all but the dgamma column
+// partials, which are laid out per 128-token wave tile).
+template <class Epi>
+struct AnyWaveWidth : std::true_type {};
+template <bool A, bool B, bool C>
+struct AnyWaveWidth<EpiRowscaleBwd<A, B, C>> : std::false_type {};
+
+// Tile-count quantization.  One 256x256 tile per CU at a time: when the tile
+// count leaves the last round of tiles partly empty (8192 x 3072 has 384
+// tiles = 1.5 rounds on 256 CUs), the trailing feature range can instead be
+// covered by 256-feature x 128-token tiles, two per big tile, each taking
+// about 0.6 of a big tile's time (measured on 8192 x 3072 x 2048).  Returns
+// the number of 256-wide feature tiles to keep in big tiles (the rest go to
+// the half tiles), or 0 to keep every tile big.  Cost model in rounds: a big
+// round is 1, a half-tile round 0.6; a split must save at least 0.2 rounds.
+inline int quantization_split(int nTF, int nTT, int nTT_half, int cus) {
+  if (cus <= 0 || nTF < 2) return 0;
+  const double base = (double)cdiv(nTF * nTT, cus);
+  double best = base - 0.2;
+  int split = 0;
+  for (int f1 = 1; f1 < nTF; ++f1) {
+    const double c = (double)cdiv(f1 * nTT, cus) + 0.6 * (double)cdiv((nTF - f1) * nTT_half, cus);
+    if (c < best) {
+      best = c;
+      split = f1;
+    }
+  }
+  return split;
+}
+
+template <bool WK, bool XK, int BT = 256, class Epi>
+coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, int F, int T, int K,
+                        const Epi& epi, hipStream_t stream) {
+  constexpr int BF = 256;
+  Problem p;
+  p.W = W;
+  p.X = X;
+  p.ldw = ldw;
+  p.ldx = ldx;
+  p.F = F;
+  p.T = T;
+  p.K = K;
+  p.nTF = cdiv(F, BF);
+  p.nTT = cdiv(T, BT);
+  p.f_base = 0;
+  const int nb = p.nTF * p.nTT;
+  if (nb == 0) return CODA_OK;
+  if constexpr (BT == 256 && XK && AnyWaveWidth<Epi>::value) {
+    const int cus = device_cus();
+    const int split = coda_tile_split(F, T, cus);
+    if (split > 0) {
+      Problem big = p, half = p;
+      big.nTF = split;
+      half.f_base = split * BF;
+      half.nTF = p.nTF - split;
+      half.nTT = cdiv(T, 128);
+      hipLaunchKernelGGL((gemm_epi_kernel_split<WK, XK, Epi>), dim3(big.nTF * big.nTT + half.nTF * half.nTT),
+                         dim3(NT), 0, stream, big, half, epi);
+      return launched();
+    }
+    // Under half a round of big tiles: 256 x 128 tiles run on twice as many
+    // CUs in the same single round, so each CU's k-loop and epilogue (the
+    // whole cost of a small GEMM) are about half as long.
+    if (cus > 0 && 2 * nb <= cus && cdiv(T, 128) > p.nTT) {
+      Problem none = p, half = p;
+      none.nTF = 0;
+      half.nTT = cdiv(T, 128);
+      hipLaunchKernelGGL((gemm_epi_kernel_split<WK, XK, Epi>), dim3(half.nTF * half.nTT), dim3(NT), 0,
+                         stream, none, half, epi);
+      return launched();
+    }
+  }
+  hipLaunchKernelGGL((gemm_epi_kernel<BF, BT, WK, XK, Epi>), dim3(nb), dim3(NT), 0, stream, p, epi);
+  return launched();
+}
+
+}  // namespace coda_launch
