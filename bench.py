@@ -3,20 +3,30 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--out FILE]
 
-One step = one pass of the fused GEMM -> residual -> RMSNorm -> GEMM forward
-at the Llama-3-1B-like shape (M = 8192 tokens, d = 2048) on seeded synthetic
-bf16 inputs already resident in HBM:
+One step = the whole 8B-like non-attention block (the largest of the five
+synthetic workloads: M = 8192 tokens, d = 4096, ffn = 14336), forward and
+reverse-fused backward, on seeded synthetic bf16 inputs already resident in
+HBM:
 
-  coda_gemm_res_sumsq  u = x W0 + z, h2 = u*gamma, sum-of-squares partials  (8192 x 2048 x 2048)
-  coda_row_rms         r = 1/sqrt(sum/d + eps)                             (aux, 8192 x 16)
-  coda_gemm_rowscale   y = r * (h2 W1)                                     (8192 x 2048 x 2048)
-  coda_gemm_rope       y_qkv = rope(r * (h2 W1qkv)), Q and K rotated        (8192 x 3072 x 2048)
+  forward   u1 = x W0 + z (+ sum-of-squares partials)      coda_gemm_res_sumsq  8192 x 4096 x 4096
+            r1 = 1/sqrt(sum/d + eps)                        coda_row_rms
+            a1 = SwiGLU(r1 (h2_1 Wgu1)), pre1 kept          coda_gemm_swiglu     8192 x 28672 x 4096
+            u2 = a1 Wd1 + u1 (+ partials), r2               coda_gemm_res_sumsq  8192 x 4096 x 14336
+            a2 = SwiGLU(r2 (h2_2 Wgu2)); out = a2 Wd2 + u2  (same calls)
+  backward  per layer (2, then 1): dWd = a^T dres; dpre = dSwiGLU(dres Wd^T) with s partials;
+            s; du = dres + r(G*gamma) - r^2 s u with n2 and dgamma partials (G = dpre Wgu^T);
+            dgamma; dWgu = n2^T dpre; finally dx = du1 W0^T and dW0 = x^T du1.
 
-The metric counts only the GEMMs' algorithmic 2*M*N*K FLOPs.  Each kernel is
-timed with HIP events recorded on the stream it is launched on, inside the
-timed region.  Rank 0 prints ONE JSON line on stdout; tables go to stderr.
-``--all`` also measures every fused call of the five synthetic workloads
-against the plain GEMM of the same shape and writes them to ``--out``.
+The metric counts only the GEMMs' algorithmic 2*M*N*K FLOPs (18.14 TFLOP per
+step).  The dominant kernel (the call with the largest time per step in the
+warmup) is timed with HIP events recorded on its launch stream around every
+one of its launches inside the timed region; that gives the roofline entry.
+Rank 0 prints ONE JSON line on stdout; tables go to stderr.  The line also
+carries the unfused sequence of the same block, the config-2 (1B) block
+forward as a secondary workload, the measured matrix-core clock, and the fp64
+oracle timed on the host on a bounded sample of the same block.  ``--all``
+also measures every fused call of the five synthetic workloads against the
+plain GEMM of the same shape and writes them to ``--out``.
 """
 
 from __future__ import annotations
@@ -76,16 +86,20 @@ class OpTimer:
         self.ev.setdefault(name, []).append((s, e))
         return out
 
+    def times_ms(self):
+        return {k: [s.elapsed_time(e) for s, e in v] for k, v in self.ev.items()}
+
     def mean_ms(self):
-        return {k: float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in self.ev.items()}
+        return {k: float(np.mean(t)) for k, t in self.times_ms().items()}
 
     def stats_ms(self):
-        """Per op: (mean, median, min) over the recorded launches."""
-        out = {}
-        for k, v in self.ev.items():
-            t = [s.elapsed_time(e) for s, e in v]
-            out[k] = (float(np.mean(t)), float(np.median(t)), float(np.min(t)))
-        return out
+        """Per op: (mean, median, min, launches) over the recorded launches."""
+        return {k: (float(np.mean(t)), float(np.median(t)), float(np.min(t)), len(t))
+                for k, t in self.times_ms().items()}
+
+
+def bare(name, fn):
+    return fn()
 
 
 def time_fn(torch, fn, iters=20, warmup=5):
@@ -105,8 +119,172 @@ def time_fn(torch, fn, iters=20, warmup=5):
     return float(np.median(times)), float(np.min(times))
 
 
+def timed_steps(torch, step, steps, tm=None):
+    """`steps` back-to-back steps between two events; returns ms per step."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        step(tm)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 # ----------------------------------------------------------------------------
-# config-2 step
+# the 8B-like block (config 5): forward + reverse-fused backward
+# ----------------------------------------------------------------------------
+
+BLOCK_DIMS = (8192, 4096, 14336)  # tokens M, model width d, ffn width F
+
+
+def block_op_flops(M, d, F):
+    """Algorithmic 2*M*N*K FLOPs per launch of each GEMM call of the step."""
+    return {
+        "res_sumsq W0": 2.0 * M * d * d,
+        "swiglu": 2.0 * M * 2 * F * d,
+        "down+res_sumsq": 2.0 * M * d * F,
+        "down+residual": 2.0 * M * d * F,
+        "wgrad dWd": 2.0 * F * d * M,
+        "swiglu_bwd+s": 2.0 * M * F * d,
+        "rowscale_bwd": 2.0 * M * d * 2 * F,
+        "wgrad dWgu": 2.0 * d * 2 * F * M,
+        "dgrad+wgrad W0": 2 * 2.0 * M * d * d,
+    }
+
+
+# launches per step of each GEMM call
+BLOCK_LAUNCHES = {"res_sumsq W0": 1, "swiglu": 2, "down+res_sumsq": 1, "down+residual": 1, "wgrad dWd": 2,
+                  "swiglu_bwd+s": 2, "rowscale_bwd": 2, "wgrad dWgu": 2, "dgrad+wgrad W0": 1}
+
+BLOCK_SHAPES = {  # (M, N, K) of each call's GEMM as the user sees it
+    "res_sumsq W0": "8192x4096x4096", "swiglu": "8192x28672x4096", "down+res_sumsq": "8192x4096x14336",
+    "down+residual": "8192x4096x14336", "wgrad dWd": "14336x4096x8192 (reduction over tokens)",
+    "swiglu_bwd+s": "8192x14336x4096", "rowscale_bwd": "8192x4096x28672",
+    "wgrad dWgu": "4096x28672x8192 (reduction over tokens)", "dgrad+wgrad W0": "8192x4096x4096 twice",
+}
+
+BLOCK_KERNELS = {  # C entry point of each call
+    "res_sumsq W0": "coda_gemm_res_sumsq", "swiglu": "coda_gemm_swiglu", "down+res_sumsq": "coda_gemm_res_sumsq",
+    "down+residual": "coda_gemm_res_sumsq", "wgrad dWd": "coda_gemm_wgrad", "swiglu_bwd+s": "coda_gemm_swiglu_bwd",
+    "rowscale_bwd": "coda_gemm_rowscale_bwd", "wgrad dWgu": "coda_gemm_wgrad",
+    "dgrad+wgrad W0": "coda_gemm_res_sumsq_bwd",
+}
+
+
+def block_inputs_device(torch, synth, M, d, F, config=5):
+    """Seeded synthetic inputs of the block (synth.block_inputs), on the GPU."""
+    p = synth.block_inputs(config, M, d, F)
+    T = {k: v.torch("cuda") for k, v in p.items() if hasattr(v, "bits")}
+    return p, T
+
+
+def make_block(torch, coda, T, M, d, F, eps):
+    """The fused step and the unfused step of the block on the tensors T.
+    Each step takes an optional OpTimer (None: bare launches)."""
+    bf, f32 = torch.bfloat16, torch.float32
+
+    def emp(*shape, dtype=bf):
+        return torch.empty(*shape, dtype=dtype, device="cuda")
+
+    A = [dict(u=emp(M, d), h=emp(M, d), part=emp(M, coda.coda_nparts(d), dtype=f32), r=emp(M, dtype=f32),
+              pre=emp(M, 2 * F), a=emp(M, F), dpre=emp(M, 2 * F), du=emp(M, d), n2=emp(M, d),
+              sp=emp(M, coda.coda_nparts(F), dtype=f32), s=emp(M, dtype=f32),
+              gp=emp(coda.coda_mparts(M), d, dtype=f32), gpu=emp(coda.coda_unfused_rmsnorm_bwd_parts(M), d, dtype=f32),
+              dg=emp(d, dtype=f32), dWgu=emp(d, 2 * F, dtype=f32), dWd=emp(F, d, dtype=f32), da=emp(M, F),
+              G=emp(M, d)) for _ in range(2)]
+    out, dx, dW0, Y0, Tm = emp(M, d), emp(M, d), emp(d, d, dtype=f32), emp(M, d), emp(M, d)
+    Lw = [dict(g=T["gamma1"], Wgu=T["Wgu1"], Wd=T["Wd1"]), dict(g=T["gamma2"], Wgu=T["Wgu2"], Wd=T["Wd2"])]
+    x, z, dOut, W0 = T["x"], T["z"], T["dOut"], T["W0"]
+
+    def fused(tm=None):
+        run = tm.run if tm is not None else bare
+        a1, a2 = A
+        run("res_sumsq W0", lambda: coda.coda_gemm_res_sumsq(x, W0, z, Lw[0]["g"], a1["u"], a1["h"], a1["part"]))
+        run("row_rms", lambda: coda.coda_row_rms(a1["part"], d, eps, a1["r"]))
+        run("swiglu", lambda: coda.coda_gemm_swiglu(a1["h"], Lw[0]["Wgu"], a1["r"], a1["a"], a1["pre"]))
+        run("down+res_sumsq", lambda: coda.coda_gemm_res_sumsq(a1["a"], Lw[0]["Wd"], a1["u"], Lw[1]["g"], a2["u"],
+                                                                 a2["h"], a2["part"]))
+        run("row_rms", lambda: coda.coda_row_rms(a2["part"], d, eps, a2["r"]))
+        run("swiglu", lambda: coda.coda_gemm_swiglu(a2["h"], Lw[1]["Wgu"], a2["r"], a2["a"], a2["pre"]))
+        run("down+residual", lambda: coda.coda_gemm_res_sumsq(a2["a"], Lw[1]["Wd"], a2["u"], U=out, want_part=False))
+        dres = dOut
+        for l in (1, 0):
+            c, W = A[l], Lw[l]
+            run("wgrad dWd", lambda: coda.coda_gemm_wgrad(c["a"], dres, c["dWd"]))
+            run("swiglu_bwd+s", lambda: coda.coda_gemm_swiglu_bwd(dres, W["Wd"], c["pre"], c["dpre"], c["sp"]))
+            run("row_rms_bwd", lambda: coda.coda_row_rms_bwd(c["sp"], d, c["s"]))
+            run("rowscale_bwd", lambda: coda.coda_gemm_rowscale_bwd(c["dpre"], W["Wgu"], c["u"], W["g"], c["r"],
+                                                                    c["s"], dres, c["du"], c["n2"], c["gp"]))
+            run("col_reduce", lambda: coda.coda_col_reduce(c["gp"], c["dg"]))
+            run("wgrad dWgu", lambda: coda.coda_gemm_wgrad(c["n2"], c["dpre"], c["dWgu"]))
+            dres = c["du"]
+        run("dgrad+wgrad W0", lambda: coda.coda_gemm_res_sumsq_bwd(A[0]["du"], W0, X=x, dX=dx, dW=dW0))
+
+    def unfused(tm=None):
+        run = tm.run if tm is not None else bare
+        a1, a2 = A
+        run("gemm W0", lambda: coda.coda_gemm(x, W0, Y0))
+        run("add_rmsnorm", lambda: coda.coda_unfused_add_rmsnorm(Y0, z, Lw[0]["g"], eps, a1["u"], a1["n2"], a1["r"]))
+        run("gemm gate/up", lambda: coda.coda_gemm(a1["n2"], Lw[0]["Wgu"], a1["pre"]))
+        run("swiglu", lambda: coda.coda_unfused_swiglu(a1["pre"], a1["a"]))
+        run("gemm down", lambda: coda.coda_gemm(a1["a"], Lw[0]["Wd"], Tm))
+        run("add_rmsnorm", lambda: coda.coda_unfused_add_rmsnorm(Tm, a1["u"], Lw[1]["g"], eps, a2["u"], a2["n2"],
+                                                                 a2["r"]))
+        run("gemm gate/up", lambda: coda.coda_gemm(a2["n2"], Lw[1]["Wgu"], a2["pre"]))
+        run("swiglu", lambda: coda.coda_unfused_swiglu(a2["pre"], a2["a"]))
+        run("gemm down", lambda: coda.coda_gemm(a2["a"], Lw[1]["Wd"], Tm))
+        run("add", lambda: coda.coda_unfused_add(Tm, a2["u"], out))
+        dres = dOut
+        for l in (1, 0):
+            c, W = A[l], Lw[l]
+            run("wgrad dWd", lambda: coda.coda_gemm_wgrad(c["a"], dres, c["dWd"]))
+            run("dgrad down", lambda: coda.coda_gemm_res_sumsq_bwd(dres, W["Wd"], dX=c["da"], want_dw=False))
+            run("swiglu_bwd", lambda: coda.coda_unfused_swiglu_bwd(c["da"], c["pre"], c["dpre"]))
+            run("dgrad gate/up", lambda: coda.coda_gemm_res_sumsq_bwd(c["dpre"], W["Wgu"], dX=c["G"], want_dw=False))
+            run("rmsnorm_bwd", lambda: coda.coda_unfused_rmsnorm_bwd(c["G"], c["u"], W["g"], c["r"], dres, c["du"],
+                                                                     c["gpu"]))
+            run("col_reduce", lambda: coda.coda_col_reduce(c["gpu"], c["dg"]))
+            run("wgrad dWgu", lambda: coda.coda_gemm_wgrad(c["n2"], c["dpre"], c["dWgu"]))
+            dres = c["du"]
+        run("dgrad+wgrad W0", lambda: coda.coda_gemm_res_sumsq_bwd(A[0]["du"], W0, X=x, dX=dx, dW=dW0))
+
+    tensors = list(T.values()) + [v for a in A for v in a.values()] + [out, dx, dW0]
+    ws_bytes = sum(t.numel() * t.element_size() for t in tensors)
+    return fused, unfused, ws_bytes
+
+
+def block_cpu_baseline(p, M, d, F, rows=256, min_seconds=12.0, max_steps=20):
+    """The fp64 oracle's block forward + backward timed on the host, on a
+    bounded sample of the same workload: the first `rows` tokens of the same
+    seeded inputs with the full weights (at least min_seconds, at most
+    max_steps steps)."""
+    from oracle import coda_oracle as O
+    from threadpoolctl import threadpool_info
+
+    q = {k: (v.f64() if hasattr(v, "bits") else v) for k, v in p.items()}
+    for k in ("x", "z", "dOut"):
+        q[k] = q[k][:rows]
+    flops = sum(block_op_flops(rows, d, F)[k] * BLOCK_LAUNCHES[k] for k in BLOCK_LAUNCHES)
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        f = O.block_fwd(q)
+        O.block_bwd(q, f)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or steps >= max_steps:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(flops * steps / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{steps} whole block forward+backward steps (W0 + 2 residual/RMSNorm/SwiGLU layers, d={d}, "
+                      f"ffn={F}, full weights) on the first {rows} of the {M} tokens, {flops / 1e12:.3f} TFLOP "
+                      f"each, fp64 numpy, {el:.1f} s"}
+
+
+# ----------------------------------------------------------------------------
+# config-2 step (the Llama-3-1B-like block forward): a secondary workload
 # ----------------------------------------------------------------------------
 
 
@@ -137,7 +315,7 @@ def make_c2_step(torch, coda, T, dims, eps):
     }
 
     def step(tm=None):
-        run = tm.run if tm is not None else (lambda n, f: f())
+        run = tm.run if tm is not None else bare
         run("res_sumsq", lambda: coda.coda_gemm_res_sumsq(T["x"], T["W0"], T["z"], T["gamma"], U=buf["U"],
                                                            H2=buf["H2"], part=buf["part"]))
         run("row_rms", lambda: coda.coda_row_rms(buf["part"], d, eps, r=buf["r"]))
@@ -163,7 +341,7 @@ def make_c2_unfused_step(torch, coda, T, dims, eps, n_rope):
     }
 
     def step(tm=None):
-        run = tm.run if tm is not None else (lambda n, f: f())
+        run = tm.run if tm is not None else bare
         run("gemm0", lambda: coda.coda_gemm(T["x"], T["W0"], buf["Y0"]))
         run("add_rmsnorm", lambda: coda.coda_unfused_add_rmsnorm(buf["Y0"], T["z"], T["gamma"], eps, U=buf["U"],
                                                                  N2=buf["N2"], r=buf["r"]))
@@ -174,9 +352,8 @@ def make_c2_unfused_step(torch, coda, T, dims, eps, n_rope):
     return step
 
 
-def cold_cache(torch, coda, synth, p, T, dims, n_rope, total_flops, min_bytes=600 << 20, steps=30):
-    """Fused step with the inputs rotated over enough copies to exceed the MALL."""
-    M, d, K, N, NR = dims
+def c2_cold_cache(torch, coda, T, dims, eps, total_flops, min_bytes=600 << 20, steps=30):
+    """Config-2 step with the inputs rotated over enough copies to exceed the MALL."""
     keys = ("x", "W0", "z", "gamma", "W1", "W1r")
     per_set = sum(T[k].numel() * T[k].element_size() for k in keys)
     nsets = max(2, -(-min_bytes // per_set))
@@ -185,7 +362,7 @@ def cold_cache(torch, coda, synth, p, T, dims, n_rope, total_flops, min_bytes=60
         Ti = dict(T)
         for k in keys:
             Ti[k] = T[k].clone()
-        sets.append(make_c2_step(torch, coda, Ti, dims, p["eps"])[0])
+        sets.append(make_c2_step(torch, coda, Ti, dims, eps)[0])
     for st in sets:
         st()
     torch.cuda.synchronize()
@@ -201,32 +378,87 @@ def cold_cache(torch, coda, synth, p, T, dims, n_rope, total_flops, min_bytes=60
             "bytes_rotated": int(nsets * per_set), "steps": steps}
 
 
-def cpu_baseline(p, dims, n_rope, min_seconds=12.0, max_steps=60):
-    """The fp64 oracle timed on the host on whole config-2 steps (at least
-    min_seconds, at most max_steps: about 12-30 s of host work)."""
-    from oracle import coda_oracle as O
-    from threadpoolctl import threadpool_info
-
+def bench_c2(torch, coda, synth, steps=100, warmup=20):
+    """The config-2 block forward: fused step, per-op times, unfused sequence, cold cache."""
+    p, T, dims = c2_inputs(torch, synth)
     M, d, K, N, NR = dims
-    x, W0, z, g, W1, W1r = (p[k].f64() for k in ("x", "W0", "z", "gamma", "W1", "W1r"))
-    pos = p["pos"]
-    flops = sum(c2_flops(*dims).values())
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        u, h2, ss = O.res_sumsq(x, W0, z, g)
-        n2, r = O.rmsnorm(u, g, p["eps"])
-        y = O.gemm(n2, W1)
-        yr = O.rope(O.gemm(n2, W1r), pos, 500000.0, 64, n_rope)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds or steps >= max_steps:
+    step, buf, n_rope = make_c2_step(torch, coda, T, dims, p["eps"])
+    flops = c2_flops(*dims)
+    total = sum(flops.values())
+    for _ in range(warmup):
+        step()
+    ms = timed_steps(torch, step, steps)
+    tm = OpTimer(torch)
+    for _ in range(steps):
+        step(tm)
+    torch.cuda.synchronize()
+    ops = {}
+    for k, (mean, med, mn, n) in tm.stats_ms().items():
+        ent = {"us": round(mean * 1e3, 2), "us_median": round(med * 1e3, 2), "us_min": round(mn * 1e3, 2)}
+        if k in flops:
+            tf = flops[k] / (mean * 1e-3) / 1e12
+            ent.update(tflops=round(tf, 1), pct_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2))
+        if k == "row_rms":
+            nb = M * coda.coda_nparts(d) * 4 + M * 4
+            ent.update(bytes=nb, gbs=round(nb / (mean * 1e-3) / 1e9, 1),
+                       pct_hbm=round(100 * nb / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 2))
+        ops[k] = ent
+    ustep = make_c2_unfused_step(torch, coda, T, dims, p["eps"], n_rope)
+    for _ in range(warmup):
+        ustep()
+    ums = timed_steps(torch, ustep, steps)
+    cold = c2_cold_cache(torch, coda, T, dims, p["eps"], total)
+    res = {
+        "workload": "GEMM->residual->RMSNorm->GEMM forward, Llama-3-1B-like: M=8192 tokens (4x2048), d=2048, "
+                    "W1 2048x2048 (rowscale) and QKV W1 2048x3072 with RoPE (theta=5e5, hd=64)",
+        "gflop_per_step": round(total / 1e9, 2), "steps": steps, "ms_per_step": round(ms, 5),
+        "value": round(total / (ms * 1e-3) / 1e12, 2), "pct_peak": round(100 * total / (ms * 1e-3) / 1e12 /
+                                                                         PEAK_BF16_TFLOPS, 2),
+        "ops": ops,
+        "unfused": {"ms_per_step": round(ums, 5), "fused_speedup": round(ums / ms, 4)},
+        "cold_cache": cold,
+    }
+    del T, buf
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------
+# the matrix-core clock of this device, measured
+# ----------------------------------------------------------------------------
+
+
+def mfma_probe(torch, coda, cus, iters=20000):
+    coda.coda_probe_mfma(cus, 100)  # warm
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    out = coda.coda_probe_mfma(cus, iters)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    t = out.double().cpu().numpy()
+    mem, real = float(np.mean(t[:, 0])), float(np.mean(t[:, 1]))
+    flops = cus * 4 * iters * 8 * 32768.0
+    ref_mhz = real / (ms * 1e3)  # reference ticks per microsecond of the event-timed launch
+    return {"sclk_mhz": round(mem / real * 100.0, 1), "refclk_mhz_check": round(ref_mhz, 2),
+            "mfma_only_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "note": "s_memtime / s_memrealtime ticks (reference clock 100 MHz) over an MFMA-only loop on every CU "
+                    f"({iters} x 8 bf16 32x32x16 MFMAs per wave); refclk_mhz_check = reference ticks per event-timed "
+                    "microsecond"}
+
+
+def device_info(torch):
+    pr = torch.cuda.get_device_properties(0)
+    rocm = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(path):
+            with open(path) as f:
+                rocm = f.read().strip()
             break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(flops * steps / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{steps} whole config-2 steps (M=8192, d=2048; 240.5 GFLOP each) in fp64 numpy, "
-                      f"{el:.1f} s"}
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "cus": pr.multi_processor_count,
+            "hbm_gib": round(pr.total_memory / 2 ** 30, 1), "rocm": rocm, "hip_runtime": torch.version.hip,
+            "torch": torch.__version__}
 
 
 def load_traffic(kernel_key):
@@ -509,7 +741,7 @@ def bench_sequences(torch, coda, iters=20):
     seq(5, "layer backward (SwiGLU MLP + RMSNorm)", 2.0 * M * d * F * 2 + 2 * 2.0 * M * d * 2 * F, f_l, u_l, 5)
     del dOut, Wd, Wgu, pre, act, u, N2, gam, r, dpre, da, G, dU, N2f, spart, s_, gpart, gpu_, dg, dWgu, dWd
     torch.cuda.empty_cache()
-    rows += bench_block(torch, coda, seq_fn=seq)
+    bench_block(torch, coda, seq)
     return rows
 
 
@@ -517,78 +749,13 @@ def bench_block(torch, coda, seq_fn):
     """The whole config-5 block (W0 projection + two residual/RMSNorm/SwiGLU-MLP
     layers), forward and backward as one stream ("CODA" paper Figure 11):
     the fused calls against the unfused sequence."""
-    bf, f32 = torch.bfloat16, torch.float32
-    M, d, F, eps = 8192, 4096, 14336, 1e-6
+    from gemm_epilogue_transformer_mainloop_amd import synth
 
-    def rnd(*shape, std=1.0):
-        return (torch.randn(*shape, device="cuda") * std).to(bf)
-
-    def emp(*shape, dtype=bf):
-        return torch.empty(*shape, dtype=dtype, device="cuda")
-
-    x, z, dOut, W0 = rnd(M, d), rnd(M, d), rnd(M, d), rnd(d, d, std=d ** -0.5)
-    L = [dict(g=(1.0 + 0.1 * torch.randn(d, device="cuda")).to(bf), Wgu=rnd(d, 2 * F, std=d ** -0.5),
-              Wd=rnd(F, d, std=F ** -0.5)) for _ in range(2)]
-    # activations (shared shapes by both paths) and gradients
-    A = [dict(u=emp(M, d), h=emp(M, d), part=emp(M, coda.coda_nparts(d), dtype=f32), r=emp(M, dtype=f32),
-              pre=emp(M, 2 * F), a=emp(M, F), dpre=emp(M, 2 * F), du=emp(M, d), n2=emp(M, d),
-              sp=emp(M, coda.coda_nparts(F), dtype=f32), s=emp(M, dtype=f32),
-              gp=emp(coda.coda_mparts(M), d, dtype=f32), gpu=emp(coda.coda_unfused_rmsnorm_bwd_parts(M), d, dtype=f32),
-              dg=emp(d, dtype=f32), dWgu=emp(d, 2 * F, dtype=f32), dWd=emp(F, d, dtype=f32), da=emp(M, F),
-              G=emp(M, d), y=emp(M, d)) for _ in range(2)]
-    out, dx, dW0, Y0, T = emp(M, d), emp(M, d), emp(d, d, dtype=f32), emp(M, d), emp(M, d)
-
-    def fused():
-        a1, a2 = A
-        coda.coda_gemm_res_sumsq(x, W0, z, L[0]["g"], a1["u"], a1["h"], a1["part"])
-        coda.coda_row_rms(a1["part"], d, eps, a1["r"])
-        coda.coda_gemm_swiglu(a1["h"], L[0]["Wgu"], a1["r"], a1["a"], a1["pre"])
-        coda.coda_gemm_res_sumsq(a1["a"], L[0]["Wd"], a1["u"], L[1]["g"], a2["u"], a2["h"], a2["part"])
-        coda.coda_row_rms(a2["part"], d, eps, a2["r"])
-        coda.coda_gemm_swiglu(a2["h"], L[1]["Wgu"], a2["r"], a2["a"], a2["pre"])
-        coda.coda_gemm_res_sumsq(a2["a"], L[1]["Wd"], a2["u"], U=out, want_part=False)
-        dres = dOut
-        for l in (1, 0):
-            c, W = A[l], L[l]
-            coda.coda_gemm_wgrad(c["a"], dres, c["dWd"])
-            coda.coda_gemm_swiglu_bwd(dres, W["Wd"], c["pre"], c["dpre"], c["sp"])
-            coda.coda_row_rms_bwd(c["sp"], d, c["s"])
-            coda.coda_gemm_rowscale_bwd(c["dpre"], W["Wgu"], c["u"], W["g"], c["r"], c["s"], dres, c["du"], c["n2"],
-                                        c["gp"])
-            coda.coda_col_reduce(c["gp"], c["dg"])
-            coda.coda_gemm_wgrad(c["n2"], c["dpre"], c["dWgu"])
-            dres = c["du"]
-        coda.coda_gemm_res_sumsq_bwd(A[0]["du"], W0, X=x, dX=dx, dW=dW0)
-
-    def unfused():
-        a1, a2 = A
-        coda.coda_gemm(x, W0, Y0)
-        coda.coda_unfused_add_rmsnorm(Y0, z, L[0]["g"], eps, a1["u"], a1["n2"], a1["r"])
-        coda.coda_gemm(a1["n2"], L[0]["Wgu"], a1["pre"])
-        coda.coda_unfused_swiglu(a1["pre"], a1["a"])
-        coda.coda_gemm(a1["a"], L[0]["Wd"], T)
-        coda.coda_unfused_add_rmsnorm(T, a1["u"], L[1]["g"], eps, a2["u"], a2["n2"], a2["r"])
-        coda.coda_gemm(a2["n2"], L[1]["Wgu"], a2["pre"])
-        coda.coda_unfused_swiglu(a2["pre"], a2["a"])
-        coda.coda_gemm(a2["a"], L[1]["Wd"], T)
-        coda.coda_unfused_add(T, a2["u"], out)
-        dres = dOut
-        for l in (1, 0):
-            c, W = A[l], L[l]
-            coda.coda_gemm_wgrad(c["a"], dres, c["dWd"])
-            coda.coda_gemm_res_sumsq_bwd(dres, W["Wd"], dX=c["da"], want_dw=False)
-            coda.coda_unfused_swiglu_bwd(c["da"], c["pre"], c["dpre"])
-            coda.coda_gemm_res_sumsq_bwd(c["dpre"], W["Wgu"], dX=c["G"], want_dw=False)
-            coda.coda_unfused_rmsnorm_bwd(c["G"], c["u"], W["g"], c["r"], dres, c["du"], c["gpu"])
-            coda.coda_col_reduce(c["gpu"], c["dg"])
-            coda.coda_gemm_wgrad(c["n2"], c["dpre"], c["dWgu"])
-            dres = c["du"]
-        coda.coda_gemm_res_sumsq_bwd(A[0]["du"], W0, X=x, dX=dx, dW=dW0)
-
-    fwd = 2.0 * M * d * d + 2 * (2.0 * M * d * 2 * F + 2.0 * M * F * d)
-    rows = []
-    seq_fn(5, "block forward+backward (W0 + 2 layers)", 3 * fwd, fused, unfused, 3)
-    return rows
+    M, d, F = BLOCK_DIMS
+    _, T = block_inputs_device(torch, synth, M, d, F)
+    fused, unfused, _ = make_block(torch, coda, T, M, d, F, 1e-6)
+    total = sum(block_op_flops(M, d, F)[k] * BLOCK_LAUNCHES[k] for k in BLOCK_LAUNCHES)
+    seq_fn(5, "block forward+backward (W0 + 2 layers)", total, lambda: fused(), lambda: unfused(), 3)
 
 
 # ----------------------------------------------------------------------------
@@ -597,11 +764,13 @@ def bench_block(torch, coda, seq_fn):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--all", action="store_true", help="also time every fused call of the five workloads")
     ap.add_argument("--out", default=None, help="file for the --all table (JSON lines)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="headline step only (no unfused sequence, config-2 block, clock probe)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -631,100 +800,40 @@ def main():
         log(f"copy calibration: 3 x {n} bytes read + {n} bytes written")
         return
 
-    p, T, dims = c2_inputs(torch, synth)
-    M, d, K, N, NR = dims
-    step, buf, n_rope = make_c2_step(torch, coda, T, dims, p["eps"])
-    flops = c2_flops(*dims)
-    total_flops = sum(flops.values())
+    dev = device_info(torch)
+    log(f"device: {dev}")
+    M, d, F = BLOCK_DIMS
+    p, T = block_inputs_device(torch, synth, M, d, F)
+    eps = p["eps"]
+    fused, unfused, ws_bytes = make_block(torch, coda, T, M, d, F, eps)
+    opf = block_op_flops(M, d, F)
+    total_flops = sum(opf[k] * BLOCK_LAUNCHES[k] for k in BLOCK_LAUNCHES)
 
-    for _ in range(args.warmup):
-        step()
+    # Warmup.  Its last steps (two, or one extra untimed step when there is
+    # no warmup) carry an event pair around every call, to find the call
+    # with the largest time per step: the roofline kernel.
+    nrank = min(args.warmup, 2)
+    for _ in range(args.warmup - nrank):
+        fused()
+    rank = OpTimer(torch)
+    for _ in range(max(nrank, 1)):
+        fused(rank)
     torch.cuda.synchronize()
+    per_step = {k: sum(t) / max(nrank, 1) for k, t in rank.times_ms().items()}
+    dom = max((k for k in per_step if k in opf), key=lambda k: per_step[k])
+    log("warmup ranking (ms per step): " + ", ".join(f"{k} {v:.3f}" for k, v in
+                                                     sorted(per_step.items(), key=lambda kv: -kv[1])))
 
-    # The timed region holds the K steps.  The roofline kernel (the RoPE
-    # call) is timed inside it, back to back with the other kernels: one HIP
-    # event pair around it in every tenth step (each pair delays the kernel
-    # it brackets by its dispatch after the marker, so fewer pairs disturb
-    # the step less).  An event pair around every call would make the host,
-    # not the GPU, set the pace.
-    dom = "rope"
+    # The timed region: exactly K steps, back to back.  Every launch of the
+    # roofline kernel is bracketed by an event pair on its launch stream
+    # (its launches per step are a few of about twenty, in a step of ~15 ms).
     dtm = OpTimer(torch, only={dom})
-    every = max(1, args.steps // 10)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        step(dtm if i % every == 0 else None)
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-    dom_ms = dtm.mean_ms()[dom]
-
-    # Per-op breakdown: another K steps with an event pair around every call,
-    # outside the timed region (kernels separated by the event records).
-    tm = OpTimer(torch)
-    for _ in range(args.steps):
-        step(tm)
-    torch.cuda.synchronize()
-    op_ms = tm.mean_ms()
-    op_stats = tm.stats_ms()
-
-    # The unfused sequence of the same block, same inputs, same number of
-    # steps, timed the same way.
-    ustep = make_c2_unfused_step(torch, coda, T, dims, p["eps"], n_rope)
-    for _ in range(args.warmup):
-        ustep()
-    torch.cuda.synchronize()
-    t_start.record()
-    for _ in range(args.steps):
-        ustep()
-    t_end.record()
-    torch.cuda.synchronize()
-    ums_step = t_start.elapsed_time(t_end) / args.steps
-    utm = OpTimer(torch)
-    for _ in range(args.steps):
-        ustep(utm)
-    torch.cuda.synchronize()
-    uops = {k: {"us_median": round(v[1] * 1e3, 2), "us_min": round(v[2] * 1e3, 2)}
-            for k, v in utm.stats_ms().items()}
-    log(f"unfused sequence: {ums_step * 1e3:.1f} us/step  {uops}")
-
-    # Cold cache: rotate input sets totalling more than 512 MB, so that no step
-    # finds its inputs in the 256 MB Infinity Cache.
-    cold = cold_cache(torch, coda, synth, p, T, dims, n_rope, total_flops)
-    log(f"cold cache: {cold}")
-
+    ms_step = timed_steps(torch, fused, args.steps, dtm)
+    d_mean, d_med, d_min, d_n = dtm.stats_ms()[dom]
     value = total_flops / (ms_step * 1e-3) / 1e12
-    achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
-    ops = {}
-    for k, v in op_ms.items():
-        ent = {"us": round(v * 1e3, 2), "us_median": round(op_stats[k][1] * 1e3, 2),
-               "us_min": round(op_stats[k][2] * 1e3, 2)}
-        if k in flops:
-            tf = flops[k] / (v * 1e-3) / 1e12
-            ent.update(tflops=round(tf, 1), pct_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2))
-        if k == "row_rms":  # aux reduction: algorithmic bytes (partials in, r out) per time
-            nb = M * coda.coda_nparts(d) * 4 + M * 4
-            ent.update(bytes=nb, gbs=round(nb / (v * 1e-3) / 1e9, 1),
-                       pct_hbm=round(100 * nb / (v * 1e-3) / 1e9 / PEAK_HBM_GBS, 2))
-        ops[k] = ent
-    log("per-op (HIP events on the launch stream):")
-    for k, v in ops.items():
-        log(f"  {k:10s} {v}")
-
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(p, dims, n_rope)
-        log(f"cpu oracle: {cpu}")
-
-    if args.all:
-        rows = bench_all(torch, coda, synth)
-        if args.out:
-            with open(args.out, "w") as f:
-                for r_ in rows:
-                    f.write(json.dumps(r_) + "\n")
+    achieved = opf[dom] / (d_mean * 1e-3) / 1e12
+    log(f"block fwd+bwd: {ms_step:.3f} ms/step, {value:.1f} TFLOP/s; {dom}: {d_mean * 1e3:.1f} us/launch "
+        f"({achieved:.1f} TFLOP/s)")
 
     line = {
         "metric": METRIC,
@@ -741,33 +850,93 @@ def main():
         "data": "synthetic",
         "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "config": {
-            "workload": "GEMM->residual->RMSNorm->GEMM forward, Llama-3-1B-like: M=8192 tokens (4x2048), d=2048, "
-                        "W1 2048x2048 (rowscale) and QKV W1 2048x3072 with RoPE (theta=5e5, hd=64)",
-            "M": M, "d": d, "K": K, "N": N, "N_qkv": NR, "n_rope": n_rope,
-            "calls": ["coda_gemm_res_sumsq", "coda_row_rms", "coda_gemm_rowscale", "coda_gemm_rope"],
+            "workload": "8B-like non-attention block forward + reverse-fused backward: M=8192 tokens, d=4096, "
+                        "ffn=14336, a d x d projection with residual then two residual+RMSNorm+SwiGLU-MLP layers; "
+                        "seeded synthetic bf16 (x, z, dOut ~N(0,1), weights ~N(0,1/fan_in), gamma ~N(1,0.1))",
+            "M": M, "d": d, "ffn": F, "layers": 2, "gflop_per_step": round(total_flops / 1e9, 1),
+            "calls_per_step": ["coda_gemm_res_sumsq", "coda_row_rms", "coda_gemm_swiglu", "coda_gemm_res_sumsq",
+                               "coda_row_rms", "coda_gemm_swiglu", "coda_gemm_res_sumsq",
+                               "2 x [coda_gemm_wgrad, coda_gemm_swiglu_bwd, coda_row_rms_bwd, "
+                               "coda_gemm_rowscale_bwd, coda_col_reduce, coda_gemm_wgrad]",
+                               "coda_gemm_res_sumsq_bwd"],
         },
-        "ops": ops,
-        "unfused": {
-            "ms_per_step": round(ums_step, 5),
-            "value": round(total_flops / (ums_step * 1e-3) / 1e12, 2),
-            "fused_speedup": round(ums_step / ms_step, 4),
-            "calls": ["coda_gemm", "coda_unfused_add_rmsnorm", "coda_gemm", "coda_gemm", "coda_unfused_rope"],
-            "ops": uops,
-        },
-        "cold_cache": cold,
+        "device": dev,
         "roofline": {
             "bound": "mfma",
-            "kernel": "coda_gemm_rope (8192x3072x2048)",
-            "us_per_launch": round(dom_ms * 1e3, 2),
-            "launches_timed": len(dtm.ev[dom]),
+            "kernel": f"{BLOCK_KERNELS[dom]} ({dom}, {BLOCK_SHAPES[dom]})",
+            "flop_per_launch": opf[dom],
+            "us_per_launch": round(d_mean * 1e3, 2),
+            "us_per_launch_median": round(d_med * 1e3, 2),
+            "launches_timed": d_n,
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": load_traffic("rope_c2"),
+            "traffic": load_traffic("c5 " + dom),
         },
-        "cpu_baseline": cpu,
     }
+
+    if not args.no_extra:
+        # Per-call breakdown: another K steps with an event pair around every
+        # call (outside the timed region).
+        tm = OpTimer(torch)
+        for _ in range(args.steps):
+            fused(tm)
+        torch.cuda.synchronize()
+        ops = {}
+        for k, (mean, med, mn, n) in tm.stats_ms().items():
+            ent = {"us": round(mean * 1e3, 2), "us_median": round(med * 1e3, 2), "us_min": round(mn * 1e3, 2),
+                   "launches_per_step": n // args.steps}
+            if k in opf:
+                tf = opf[k] / (mean * 1e-3) / 1e12
+                ent.update(tflops=round(tf, 1), pct_peak=round(100 * tf / PEAK_BF16_TFLOPS, 2))
+            ops[k] = ent
+        line["ops"] = ops
+        log("per-call (HIP events on the launch stream):")
+        for k, v in ops.items():
+            log(f"  {k:16s} {v}")
+        # The unfused sequence of the same block on the same tensors.
+        for _ in range(args.warmup):
+            unfused()
+        ums = timed_steps(torch, unfused, args.steps)
+        utm = OpTimer(torch)
+        for _ in range(args.steps):
+            unfused(utm)
+        torch.cuda.synchronize()
+        line["unfused"] = {
+            "ms_per_step": round(ums, 5), "value": round(total_flops / (ums * 1e-3) / 1e12, 2),
+            "fused_speedup": round(ums / ms_step, 4),
+            "ops": {k: {"us_median": round(v[1] * 1e3, 2), "launches_per_step": v[3] // args.steps}
+                    for k, v in utm.stats_ms().items()},
+        }
+        log(f"unfused block: {ums:.3f} ms/step ({ums / ms_step:.3f}x the fused step)")
+        line["cold_cache"] = {
+            "working_set_bytes": int(ws_bytes),
+            "note": f"the step touches {ws_bytes / 2 ** 30:.1f} GiB of weights, activations and gradients, far "
+                    "beyond the 256 MB Infinity Cache: every timed step runs from HBM; the config-2 entry "
+                    "carries a rotated-input cold-cache run of its smaller step"}
+        del T
+        fused = unfused = None
+        torch.cuda.empty_cache()
+        line["config2_block_forward"] = bench_c2(torch, coda, synth)
+        log(f"config-2 block forward: {line['config2_block_forward']['value']} TFLOP/s")
+        line["mfma_clock_probe"] = mfma_probe(torch, coda, dev["cus"])
+        log(f"clock probe: {line['mfma_clock_probe']}")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = block_cpu_baseline(p, M, d, F)
+        log(f"cpu oracle: {cpu}")
+    line["cpu_baseline"] = cpu
+
+    if args.all:
+        torch.cuda.empty_cache()
+        rows = bench_all(torch, coda, synth)
+        if args.out:
+            with open(args.out, "w") as f:
+                for r_ in rows:
+                    f.write(json.dumps(r_) + "\n")
+
     print(json.dumps(line), flush=True)
 
 

@@ -30,7 +30,8 @@ LIB = os.path.join(HERE, "libcoda.so")
 RESOURCES = os.path.join(HERE, "libcoda.resources.json")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["coda_aux.hip", "coda_fwd.hip", "coda_pair.hip", "coda_bwd.hip", "coda_ce.hip", "coda_unfused.hip"]
+SOURCES = ["coda_aux.hip", "coda_fwd.hip", "coda_pair.hip", "coda_bwd.hip", "coda_ce.hip", "coda_unfused.hip",
+           "coda_probe.hip"]
 OBJDIR = os.path.join(HERE, "_build")
 
 FLAGS = [

@@ -19,7 +19,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcoda.so")
 INCLUDE_DIR = os.path.join(os.path.dirname(_HERE), "include")
-HEADER_PATHS = [os.path.join(INCLUDE_DIR, h) for h in ("coda.h", "coda_unfused.h")]
+HEADER_PATHS = [os.path.join(INCLUDE_DIR, h) for h in ("coda.h", "coda_unfused.h", "coda_probe.h")]
 
 _lib = None
 
@@ -32,6 +32,7 @@ SZ = ctypes.c_size_t
 _SIGS = {
     "coda_status_str": (ctypes.c_char_p, [I]),
     "coda_version": (ctypes.c_char_p, []),
+    "coda_debug_extent": (I, [P, SZ]),
     "coda_nparts": (I, [I]),
     "coda_mparts": (I, [I]),
     "coda_tile_split": (I, [I, I, I]),
@@ -64,10 +65,12 @@ _SIGS = {
     "coda_unfused_rmsnorm_bwd": (I, [P, I, P, I, P, P, P, I, P, I, P, I, I, P]),
     "coda_unfused_cross_entropy": (I, [P, I, P, P, P, P, I, I, P]),
     "coda_unfused_cross_entropy_bwd": (I, [P, I, P, P, F, P, I, I, I, P]),
+    # include/coda_probe.h
+    "coda_probe_mfma": (I, [I, I, P, P]),
 }
 
 STATUS = {0: "CODA_OK", 1: "CODA_ERR_NULL", 2: "CODA_ERR_SHAPE", 3: "CODA_ERR_ALIGN",
-          4: "CODA_ERR_UNSUPPORTED", 5: "CODA_ERR_HIP", 6: "CODA_ERR_WORKSPACE"}
+          4: "CODA_ERR_UNSUPPORTED", 5: "CODA_ERR_HIP", 6: "CODA_ERR_WORKSPACE", 7: "CODA_ERR_BOUNDS"}
 
 
 class CodaError(RuntimeError):
@@ -92,7 +95,7 @@ def lib():
 
 
 def header_functions():
-    """Names of the functions include/coda.h and include/coda_unfused.h declare."""
+    """Names of the functions the public headers (coda.h, coda_unfused.h, coda_probe.h) declare."""
     names = set()
     for path in HEADER_PATHS:
         with open(path) as f:
@@ -166,6 +169,11 @@ def coda_lmhead_ce_workspace(M: int, V: int) -> int:
 
 def coda_lmhead_ce_bwd_workspace(M: int, V: int, d: int) -> int:
     return int(lib().coda_lmhead_ce_bwd_workspace(M, V, d))
+
+
+def coda_debug_extent(p: int, nbytes: int) -> int:
+    """CODA_DEBUG's extent check of [p, p + nbytes) (returns the status code)."""
+    return int(lib().coda_debug_extent(ctypes.c_void_p(p), nbytes))
 
 
 # ----------------------------------------------------------------------------
@@ -471,3 +479,17 @@ def coda_unfused_cross_entropy_bwd(L, labels, lse, grad_scale: float, D=None):
     _call("coda_unfused_cross_entropy_bwd", _ptr(L), _ld(L), _ptr(labels), _ptr(lse), ctypes.c_float(grad_scale),
           _ptr(D), _ld(D), M, V, _stream())
     return D
+
+
+# ----------------------------------------------------------------------------
+# measurement support (include/coda_probe.h)
+# ----------------------------------------------------------------------------
+
+
+def coda_probe_mfma(blocks: int, iters: int, out=None):
+    """Matrix-core clock probe; returns the int64 device tensor [blocks, 2] of
+    (shader-clock ticks, reference-clock ticks) per workgroup."""
+    if out is None:
+        out = torch.zeros((blocks, 2), dtype=torch.int64, device="cuda")
+    _call("coda_probe_mfma", blocks, iters, _ptr(out), _stream())
+    return out

@@ -95,11 +95,14 @@ const char* coda_status_str(coda_status s) {
     case CODA_ERR_UNSUPPORTED: return "unsupported device or parameter combination";
     case CODA_ERR_HIP: return "HIP runtime error";
     case CODA_ERR_WORKSPACE: return "workspace missing or too small";
+    case CODA_ERR_BOUNDS: return "an argument's extent leaves its device allocation (CODA_DEBUG)";
   }
   return "unknown status";
 }
 
-const char* coda_version(void) { return "coda-gfx950 0.1"; }
+const char* coda_version(void) { return "coda-gfx950 0.2"; }
+
+coda_status coda_debug_extent(const void* p, size_t bytes) { return extent_ok(p, bytes); }
 
 int coda_nparts(int N) { return N <= 0 ? 0 : cdiv(N, WAVE_F); }
 int coda_mparts(int M) { return M <= 0 ? 0 : cdiv(M, WAVE_T); }
@@ -111,39 +114,42 @@ int coda_tile_split(int F, int T, int cus) {
 
 coda_status coda_row_rms(const float* part, int nparts, int M, int d, float eps, float* r,
                          hipStream_t stream) {
+  trace("coda_row_rms", "nparts=%d M=%d d=%d eps=%g", nparts, M, d, (double)eps);
   Check c;
   c.shape(M >= 0 && nparts >= 1 && d >= 1 && eps >= 0.0f);
-  c.vec(part, true, false, M);
-  c.vec(r, true, false, M);
+  c.vec(part, (long long)M * nparts, 4);
+  c.vec(r, M, 4);
   if (c.st != CODA_OK) return c.st;
   if (M == 0) return CODA_OK;
-  if (coda_status s = device_ok()) return s;
+  if (coda_status s = c.device()) return s;
   launch_row_reduce<true>(part, nparts, M, 1.0f / (float)d, eps, r, stream);
   return launched();
 }
 
 coda_status coda_row_rms_bwd(const float* spart, int nparts, int M, int d, float* s,
                              hipStream_t stream) {
+  trace("coda_row_rms_bwd", "nparts=%d M=%d d=%d", nparts, M, d);
   Check c;
   c.shape(M >= 0 && nparts >= 1 && d >= 1);
-  c.vec(spart, true, false, M);
-  c.vec(s, true, false, M);
+  c.vec(spart, (long long)M * nparts, 4);
+  c.vec(s, M, 4);
   if (c.st != CODA_OK) return c.st;
   if (M == 0) return CODA_OK;
-  if (coda_status st = device_ok()) return st;
+  if (coda_status st = c.device()) return st;
   launch_row_reduce<false>(spart, nparts, M, 1.0f / (float)d, 0.0f, s, stream);
   return launched();
 }
 
 coda_status coda_col_reduce(const float* gpart, int mparts, int d, float* dgamma,
                             hipStream_t stream) {
+  trace("coda_col_reduce", "mparts=%d d=%d", mparts, d);
   Check c;
   c.shape(mparts >= 1 && d >= 0);
-  c.vec(gpart);
-  c.vec(dgamma);
+  c.vec(gpart, (long long)mparts * d, 4);
+  c.vec(dgamma, d, 4);
   if (c.st != CODA_OK) return c.st;
   if (d == 0) return CODA_OK;
-  if (coda_status st = device_ok()) return st;
+  if (coda_status st = c.device()) return st;
   hipLaunchKernelGGL(col_reduce_kernel, dim3(cdiv(d, CR_COLS)), dim3(256), 0, stream, gpart, mparts,
                      d, dgamma);
   return launched();

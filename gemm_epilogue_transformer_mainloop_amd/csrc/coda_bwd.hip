@@ -22,18 +22,19 @@ extern "C" {
 coda_status coda_gemm_swiglu_bwd(const coda_bf16* dOut, int ldd, const coda_bf16* Wd, int ldw,
                                  const coda_bf16* Pre, int ldp, coda_bf16* dPre, int lddp,
                                  float* spart, int M, int F, int N, hipStream_t stream) {
+  trace("coda_gemm_swiglu_bwd", "M=%d F=%d N=%d spart=%d", M, F, N, spart != nullptr);
   Check c;
   c.shape(M >= 0 && F >= 0 && N >= 0 && F <= (1 << 29));
   if (c.st != CODA_OK) return c.st;
-  c.bmat(dOut, ldd, N, true, M);
-  c.bmat(Wd, ldw, N);
-  c.bmat(Pre, ldp, 2 * F, true, M);
-  c.bmat(dPre, lddp, 2 * F, true, M);
-  c.vec(spart, false, false, M);
+  c.bmat(dOut, ldd, N, M);
+  c.bmat(Wd, ldw, N, F);
+  c.bmat(Pre, ldp, 2 * F, M);
+  c.bmat(dPre, lddp, 2 * F, M);
+  c.vec(spart, (long long)M * coda_nparts(F), 4, false);
   c.shape(F % 8 == 0 && N % 8 == 0);
   if (c.st != CODA_OK) return c.st;
   if (M == 0 || F == 0) return CODA_OK;
-  if (coda_status s = device_ok()) return s;
+  if (coda_status s = c.device()) return s;
   const int np = coda_nparts(F);
   // da[M x F] = dOut[M x N] Wd^T: features = F (rows of Wd, K-major), tokens = M.
   if (spart) {
@@ -49,22 +50,23 @@ coda_status coda_gemm_rowscale_bwd(const coda_bf16* dY, int ldd, const coda_bf16
                                    const float* r, const float* s, const coda_bf16* dRes, int ldr,
                                    coda_bf16* dU, int lddu, coda_bf16* N2, int ldn, float* gpart,
                                    int M, int d, int N, hipStream_t stream) {
+  trace("coda_gemm_rowscale_bwd", "M=%d d=%d N=%d dRes=%d N2=%d gpart=%d", M, d, N, dRes != nullptr, N2 != nullptr, gpart != nullptr);
   Check c;
   c.shape(M >= 0 && d >= 0 && N >= 0);
-  c.bmat(dY, ldd, N, true, M);
-  c.bmat(W1, ldw, N);
-  c.bmat(U, ldu, d, true, M);
-  c.vec(gamma, true, true);
-  c.vec(r, true, false, M);
-  c.vec(s, true, false, M);
-  c.bmat(dRes, ldr, d, false, M);
-  c.bmat(dU, lddu, d, true, M);
-  c.bmat(N2, ldn, d, false, M);
-  c.vec(gpart, false);
+  c.bmat(dY, ldd, N, M);
+  c.bmat(W1, ldw, N, d);
+  c.bmat(U, ldu, d, M);
+  c.vec(gamma, d, 2, true, true);
+  c.vec(r, M, 4);
+  c.vec(s, M, 4);
+  c.bmat(dRes, ldr, d, M, false);
+  c.bmat(dU, lddu, d, M);
+  c.bmat(N2, ldn, d, M, false);
+  c.vec(gpart, (long long)coda_mparts(M) * d, 4, false);
   c.shape(d % 8 == 0 && N % 8 == 0);
   if (c.st != CODA_OK) return c.st;
   if (M == 0 || d == 0) return CODA_OK;
-  if (coda_status st = device_ok()) return st;
+  if (coda_status st = c.device()) return st;
 #define CODA_RB(HR, HN, HG)                                                             \
   {                                                                                     \
     EpiRowscaleBwd<HR, HN, HG> e{U, ldu, gamma, r, s, dRes, ldr, dU, lddu, N2, ldn,     \
@@ -85,15 +87,16 @@ coda_status coda_gemm_rowscale_bwd(const coda_bf16* dY, int ldd, const coda_bf16
 
 coda_status coda_gemm_wgrad(const coda_bf16* X, int ldx, const coda_bf16* dY, int ldd, float* dW,
                             int lddw, int M, int K, int N, int accumulate, hipStream_t stream) {
+  trace("coda_gemm_wgrad", "M=%d K=%d N=%d accumulate=%d", M, K, N, accumulate);
   Check c;
   c.shape(M >= 0 && K >= 0 && N >= 0);
-  c.bmat(X, ldx, K, true, M);
-  c.bmat(dY, ldd, N, true, M);
-  c.fmat(dW, lddw, N);
+  c.bmat(X, ldx, K, M);
+  c.bmat(dY, ldd, N, M);
+  c.fmat(dW, lddw, N, K);
   c.shape(K % 8 == 0 && N % 8 == 0);
   if (c.st != CODA_OK) return c.st;
   if (K == 0 || N == 0) return CODA_OK;
-  if (coda_status st = device_ok()) return st;
+  if (coda_status st = c.device()) return st;
   // dW[K x N] = X^T dY: features = N (dY, contiguous along N -> MN-major),
   // tokens = K (X, contiguous along K -> MN-major), reduction = M.
   if (accumulate) {
@@ -108,20 +111,21 @@ coda_status coda_gemm_res_sumsq_bwd(const coda_bf16* dU, int ldu, const coda_bf1
                                     const coda_bf16* X, int ldx, const coda_bf16* dRes, int ldr,
                                     coda_bf16* dX, int lddx, float* dW, int lddw, int M, int N,
                                     int K, hipStream_t stream) {
+  trace("coda_gemm_res_sumsq_bwd", "M=%d N=%d K=%d dRes=%d dW=%d", M, N, K, dRes != nullptr, dW != nullptr);
   Check c;
   c.shape(M >= 0 && N >= 0 && K >= 0);
-  c.bmat(dU, ldu, N, true, M);
-  c.bmat(W, ldw, N);
-  c.bmat(dRes, ldr, K, false, M);
-  c.bmat(dX, lddx, K, true, M);
+  c.bmat(dU, ldu, N, M);
+  c.bmat(W, ldw, N, K);
+  c.bmat(dRes, ldr, K, M, false);
+  c.bmat(dX, lddx, K, M);
   if (dW) {
-    c.bmat(X, ldx, K, true, M);
-    c.fmat(dW, lddw, N);
+    c.bmat(X, ldx, K, M);
+    c.fmat(dW, lddw, N, K);
   }
   c.shape(N % 8 == 0 && K % 8 == 0);
   if (c.st != CODA_OK) return c.st;
   if (M == 0 && dW == nullptr) return CODA_OK;
-  if (coda_status st = device_ok()) return st;
+  if (coda_status st = c.device()) return st;
   if (M > 0 && K > 0) {
     // dX[M x K] = dU[M x N] W^T: features = K (rows of W, K-major over N).
     coda_status s2;

@@ -130,19 +130,19 @@ static coda_status lmhead_ce_common(const coda_bf16* H, int ldh, const coda_bf16
                                     hipStream_t stream) {
   Check c;
   c.shape(M >= 0 && V >= 0 && d >= 0);
-  c.bmat(H, ldh, d, true, M);
-  c.bmat(W, ldw, V);
-  c.vec(labels, true, false, M);
-  c.vec(lse, true, false, M);
-  c.vec(loss_row, false);
-  c.vec(loss_mean, false);
-  if (keep) c.bmat(logits, ldl, V, true, M);
+  c.bmat(H, ldh, d, M);
+  c.bmat(W, ldw, V, d);
+  c.vec(labels, M, 4);
+  c.vec(lse, M, 4);
+  c.vec(loss_row, M, 4, false);
+  c.vec(loss_mean, 1, 4, false);
+  if (keep) c.bmat(logits, ldl, V, M);
   c.shape(V % 8 == 0 && d % 8 == 0);
   if (c.st != CODA_OK) return c.st;
   if (M == 0 || V == 0) return CODA_OK;
   if (ws == nullptr || !al16(ws) || ws_bytes < coda_lmhead_ce_workspace(M, V))
     return CODA_ERR_WORKSPACE;
-  if (coda_status s = device_ok()) return s;
+  if (coda_status s = c.device()) return s;
   const int np = coda_nparts(V);
   float* pm = static_cast<float*>(ws);
   float* ps = pm + (size_t)M * np;
@@ -169,6 +169,7 @@ static coda_status lmhead_ce_common(const coda_bf16* H, int ldh, const coda_bf16
 coda_status coda_lmhead_ce(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
                            const int32_t* labels, float* lse, float* loss_row, float* loss_mean,
                            void* ws, size_t ws_bytes, int M, int V, int d, hipStream_t stream) {
+  trace("coda_lmhead_ce", "M=%d V=%d d=%d ws_bytes=%zu", M, V, d, ws_bytes);
   return lmhead_ce_common(H, ldh, W, ldw, labels, lse, loss_row, loss_mean, nullptr, 0, false, ws,
                           ws_bytes, M, V, d, stream);
 }
@@ -177,6 +178,7 @@ coda_status coda_lmhead_ce_logits(const coda_bf16* H, int ldh, const coda_bf16* 
                                   const int32_t* labels, float* lse, float* loss_row,
                                   float* loss_mean, coda_bf16* logits, int ldl, void* ws,
                                   size_t ws_bytes, int M, int V, int d, hipStream_t stream) {
+  trace("coda_lmhead_ce_logits", "M=%d V=%d d=%d ws_bytes=%zu", M, V, d, ws_bytes);
   return lmhead_ce_common(H, ldh, W, ldw, labels, lse, loss_row, loss_mean, logits, ldl, true, ws,
                           ws_bytes, M, V, d, stream);
 }
@@ -185,20 +187,21 @@ coda_status coda_lmhead_ce_bwd(const coda_bf16* H, int ldh, const coda_bf16* W, 
                                const int32_t* labels, const float* lse, float grad_scale,
                                coda_bf16* dH, int lddh, float* dW, int lddw, void* ws,
                                size_t ws_bytes, int M, int V, int d, hipStream_t stream) {
+  trace("coda_lmhead_ce_bwd", "M=%d V=%d d=%d ws_bytes=%zu", M, V, d, ws_bytes);
   Check c;
   c.shape(M >= 0 && V >= 0 && d >= 0);
-  c.bmat(H, ldh, d, true, M);
-  c.bmat(W, ldw, V);
-  c.vec(labels, true, false, M);
-  c.vec(lse, true, false, M);
-  c.bmat(dH, lddh, d, true, M);
-  c.fmat(dW, lddw, V);
+  c.bmat(H, ldh, d, M);
+  c.bmat(W, ldw, V, d);
+  c.vec(labels, M, 4);
+  c.vec(lse, M, 4);
+  c.bmat(dH, lddh, d, M);
+  c.fmat(dW, lddw, V, d);
   c.shape(V % 8 == 0 && d % 8 == 0);
   if (c.st != CODA_OK) return c.st;
   if (V == 0 || d == 0) return CODA_OK;
   if (M > 0 && (ws == nullptr || !al16(ws) || ws_bytes < coda_lmhead_ce_bwd_workspace(M, V, d)))
     return CODA_ERR_WORKSPACE;
-  if (coda_status st = device_ok()) return st;
+  if (coda_status st = c.device()) return st;
   if (M == 0)  // no rows: dW = H^T D over an empty reduction = 0
     return coda_gemm_wgrad(H, ldh, nullptr, V, dW, lddw, 0, d, V, 0, stream);
   // Rows per chunk: as many as the workspace holds, a multiple of 256.
@@ -228,19 +231,20 @@ coda_status coda_lmhead_ce_bwd_logits(const coda_bf16* H, int ldh, const coda_bf
                                       coda_bf16* logits, int ldl, coda_bf16* dH, int lddh,
                                       float* dW, int lddw, int M, int V, int d,
                                       hipStream_t stream) {
+  trace("coda_lmhead_ce_bwd_logits", "M=%d V=%d d=%d", M, V, d);
   Check c;
   c.shape(M >= 0 && V >= 0 && d >= 0);
-  c.bmat(H, ldh, d, true, M);
-  c.bmat(W, ldw, V);
-  c.vec(labels, true, false, M);
-  c.vec(lse, true, false, M);
-  c.bmat(logits, ldl, V, true, M);
-  c.bmat(dH, lddh, d, true, M);
-  c.fmat(dW, lddw, V);
+  c.bmat(H, ldh, d, M);
+  c.bmat(W, ldw, V, d);
+  c.vec(labels, M, 4);
+  c.vec(lse, M, 4);
+  c.bmat(logits, ldl, V, M);
+  c.bmat(dH, lddh, d, M);
+  c.fmat(dW, lddw, V, d);
   c.shape(V % 8 == 0 && d % 8 == 0);
   if (c.st != CODA_OK) return c.st;
   if (V == 0 || d == 0) return CODA_OK;
-  if (coda_status st = device_ok()) return st;
+  if (coda_status st = c.device()) return st;
   if (M == 0)  // no rows: dW = H^T D over an empty reduction = 0
     return coda_gemm_wgrad(H, ldh, nullptr, V, dW, lddw, 0, d, V, 0, stream);
   // 1) dlogits in place of the logits

@@ -358,14 +358,15 @@ extern "C" {
 
 coda_status coda_unfused_add(const coda_bf16* A, int lda, const coda_bf16* B, int ldb, coda_bf16* C, int ldc,
                              int M, int N, hipStream_t stream) {
+  trace("coda_unfused_add", "M=%d N=%d", M, N);
   Check c;
   c.shape(M >= 0 && N >= 0 && N % 8 == 0);
-  c.bmat(A, lda, N, true, M);
-  c.bmat(B, ldb, N, true, M);
-  c.bmat(C, ldc, N, true, M);
+  c.bmat(A, lda, N, M);
+  c.bmat(B, ldb, N, M);
+  c.bmat(C, ldc, N, M);
   if (c.st != CODA_OK) return c.st;
   if (M == 0 || N == 0) return CODA_OK;
-  if (coda_status s = device_ok()) return s;
+  if (coda_status s = c.device()) return s;
   hipLaunchKernelGGL(add_kernel, dim3(grid_for(nchunks(M, N))), dim3(RT), 0, stream, A, lda, B, ldb, C, ldc, M, N);
   return launched();
 }
@@ -373,19 +374,20 @@ coda_status coda_unfused_add(const coda_bf16* A, int lda, const coda_bf16* B, in
 coda_status coda_unfused_add_rmsnorm(const coda_bf16* Y, int ldy, const coda_bf16* Z, int ldz,
                                      const coda_bf16* gamma, float eps, coda_bf16* U, int ldu, coda_bf16* N2,
                                      int ldn, float* r, int M, int d, hipStream_t stream) {
+  trace("coda_unfused_add_rmsnorm", "M=%d d=%d", M, d);
   Check c;
   c.shape(M >= 0 && d >= 8 && d % 8 == 0);
   c.unsupported(d <= MAX_CHUNKS * RT * 8);
-  c.bmat(Y, ldy, d, true, M);
-  c.bmat(Z, ldz, d, false, M);
-  c.vec(gamma, true, true);
-  c.bmat(U, ldu, d, true, M);
-  c.bmat(N2, ldn, d, true, M);
-  c.vec(r, true, false, M);
+  c.bmat(Y, ldy, d, M);
+  c.bmat(Z, ldz, d, M, false);
+  c.vec(gamma, d, 2, true, true);
+  c.bmat(U, ldu, d, M);
+  c.bmat(N2, ldn, d, M);
+  c.vec(r, M, 4);
   c.shape(eps >= 0.0f);
   if (c.st != CODA_OK) return c.st;
   if (M == 0) return CODA_OK;
-  if (coda_status s = device_ok()) return s;
+  if (coda_status s = c.device()) return s;
   hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(M), dim3(RT), 0, stream, Y, ldy, Z, ldz, gamma, eps, U, ldu, N2,
                      ldn, r, d);
   return launched();
@@ -393,15 +395,16 @@ coda_status coda_unfused_add_rmsnorm(const coda_bf16* Y, int ldy, const coda_bf1
 
 coda_status coda_unfused_rope(coda_bf16* Y, int ldy, const int32_t* pos, float theta, int head_dim, int n_rope,
                               int inverse, int M, int N, hipStream_t stream) {
+  trace("coda_unfused_rope", "M=%d N=%d head_dim=%d n_rope=%d", M, N, head_dim, n_rope);
   Check c;
   c.shape(M >= 0 && N >= 0 && N % 8 == 0);
-  c.bmat(Y, ldy, N, true, M);
-  c.vec(pos, true, false, M);
+  c.bmat(Y, ldy, N, M);
+  c.vec(pos, M, 4);
   c.unsupported(head_dim >= 2 && head_dim % 2 == 0 && n_rope >= 0 && n_rope <= N && n_rope % head_dim == 0);
   c.shape(theta > 0.0f);
   if (c.st != CODA_OK) return c.st;
   if (M == 0 || N == 0 || n_rope == 0) return CODA_OK;
-  if (coda_status s = device_ok()) return s;
+  if (coda_status s = c.device()) return s;
   const int chunks = (n_rope + 7) / 8;
   const int gx = (chunks + ROPE_RC - 1) / ROPE_RC;
   const int gy = std::min((M + ROPE_RR - 1) / ROPE_RR, 16384);
@@ -412,27 +415,29 @@ coda_status coda_unfused_rope(coda_bf16* Y, int ldy, const int32_t* pos, float t
 
 coda_status coda_unfused_swiglu(const coda_bf16* Pre, int ldp, coda_bf16* Act, int lda, int M, int F,
                                 hipStream_t stream) {
+  trace("coda_unfused_swiglu", "M=%d F=%d", M, F);
   Check c;
   c.shape(M >= 0 && F >= 0 && F % 8 == 0 && F <= (1 << 29));
-  c.bmat(Pre, ldp, 2 * F, true, M);
-  c.bmat(Act, lda, F, true, M);
+  c.bmat(Pre, ldp, 2 * F, M);
+  c.bmat(Act, lda, F, M);
   if (c.st != CODA_OK) return c.st;
   if (M == 0 || F == 0) return CODA_OK;
-  if (coda_status s = device_ok()) return s;
+  if (coda_status s = c.device()) return s;
   hipLaunchKernelGGL(swiglu_kernel, dim3(grid_for(nchunks(M, F))), dim3(RT), 0, stream, Pre, ldp, Act, lda, M, F);
   return launched();
 }
 
 coda_status coda_unfused_swiglu_bwd(const coda_bf16* dA, int ldda, const coda_bf16* Pre, int ldp, coda_bf16* dPre,
                                     int lddp, int M, int F, hipStream_t stream) {
+  trace("coda_unfused_swiglu_bwd", "M=%d F=%d", M, F);
   Check c;
   c.shape(M >= 0 && F >= 0 && F % 8 == 0 && F <= (1 << 29));
-  c.bmat(dA, ldda, F, true, M);
-  c.bmat(Pre, ldp, 2 * F, true, M);
-  c.bmat(dPre, lddp, 2 * F, true, M);
+  c.bmat(dA, ldda, F, M);
+  c.bmat(Pre, ldp, 2 * F, M);
+  c.bmat(dPre, lddp, 2 * F, M);
   if (c.st != CODA_OK) return c.st;
   if (M == 0 || F == 0) return CODA_OK;
-  if (coda_status s = device_ok()) return s;
+  if (coda_status s = c.device()) return s;
   hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(grid_for(nchunks(M, F))), dim3(RT), 0, stream, dA, ldda, Pre, ldp,
                      dPre, lddp, M, F);
   return launched();
@@ -443,19 +448,20 @@ int coda_unfused_rmsnorm_bwd_parts(int M) { return M <= 0 ? 0 : cdiv(M, BWD_ROWS
 coda_status coda_unfused_rmsnorm_bwd(const coda_bf16* G, int ldg, const coda_bf16* U, int ldu,
                                      const coda_bf16* gamma, const float* r, const coda_bf16* dRes, int ldr,
                                      coda_bf16* dU, int lddu, float* gpart, int M, int d, hipStream_t stream) {
+  trace("coda_unfused_rmsnorm_bwd", "M=%d d=%d", M, d);
   Check c;
   c.shape(M >= 0 && d >= 8 && d % 8 == 0);
   c.unsupported(d <= MAX_CHUNKS * RT * 8);
-  c.bmat(G, ldg, d, true, M);
-  c.bmat(U, ldu, d, true, M);
-  c.vec(gamma, true, true);
-  c.vec(r, true, false, M);
-  c.bmat(dRes, ldr, d, false, M);
-  c.bmat(dU, lddu, d, true, M);
-  c.vec(gpart, false, true);
+  c.bmat(G, ldg, d, M);
+  c.bmat(U, ldu, d, M);
+  c.vec(gamma, d, 2, true, true);
+  c.vec(r, M, 4);
+  c.bmat(dRes, ldr, d, M, false);
+  c.bmat(dU, lddu, d, M);
+  c.vec(gpart, (long long)coda_unfused_rmsnorm_bwd_parts(M) * d, 4, false, true);
   if (c.st != CODA_OK) return c.st;
   if (M == 0) return CODA_OK;
-  if (coda_status s = device_ok()) return s;
+  if (coda_status s = c.device()) return s;
   hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(cdiv(M, BWD_ROWS)), dim3(RT), 0, stream, G, ldg, U, ldu, gamma, r,
                      dRes, ldr, dU, lddu, gpart, M, d);
   return launched();
@@ -463,15 +469,16 @@ coda_status coda_unfused_rmsnorm_bwd(const coda_bf16* G, int ldg, const coda_bf1
 
 coda_status coda_unfused_cross_entropy(const coda_bf16* L, int ldl, const int32_t* labels, float* lse,
                                        float* loss_row, float* loss_mean, int M, int V, hipStream_t stream) {
+  trace("coda_unfused_cross_entropy", "M=%d V=%d", M, V);
   Check c;
   c.shape(M >= 0 && V >= 8 && V % 8 == 0);
-  c.bmat(L, ldl, V, true, M);
-  c.vec(labels, true, false, M);
-  c.vec(lse, true, false, M);
-  c.vec(loss_row, true, false, M);
+  c.bmat(L, ldl, V, M);
+  c.vec(labels, M, 4);
+  c.vec(lse, M, 4);
+  c.vec(loss_row, M, 4);
   if (c.st != CODA_OK) return c.st;
   if (M == 0) return CODA_OK;
-  if (coda_status s = device_ok()) return s;
+  if (coda_status s = c.device()) return s;
   hipLaunchKernelGGL(ce_kernel, dim3(M), dim3(RT), 0, stream, L, ldl, labels, lse, loss_row, V);
   if (loss_mean) hipLaunchKernelGGL(mean_kernel, dim3(1), dim3(1024), 0, stream, loss_row, M, loss_mean);
   return launched();
@@ -480,15 +487,16 @@ coda_status coda_unfused_cross_entropy(const coda_bf16* L, int ldl, const int32_
 coda_status coda_unfused_cross_entropy_bwd(const coda_bf16* L, int ldl, const int32_t* labels, const float* lse,
                                            float grad_scale, coda_bf16* D, int ldd, int M, int V,
                                            hipStream_t stream) {
+  trace("coda_unfused_cross_entropy_bwd", "M=%d V=%d", M, V);
   Check c;
   c.shape(M >= 0 && V >= 8 && V % 8 == 0);
-  c.bmat(L, ldl, V, true, M);
-  c.vec(labels, true, false, M);
-  c.vec(lse, true, false, M);
-  c.bmat(D, ldd, V, true, M);
+  c.bmat(L, ldl, V, M);
+  c.vec(labels, M, 4);
+  c.vec(lse, M, 4);
+  c.bmat(D, ldd, V, M);
   if (c.st != CODA_OK) return c.st;
   if (M == 0) return CODA_OK;
-  if (coda_status s = device_ok()) return s;
+  if (coda_status s = c.device()) return s;
   hipLaunchKernelGGL(ce_bwd_kernel, dim3(grid_for(nchunks(M, V))), dim3(RT), 0, stream, L, ldl, labels, lse,
                      grad_scale, D, ldd, M, V);
   return launched();

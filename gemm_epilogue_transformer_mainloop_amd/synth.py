@@ -32,9 +32,11 @@ import numpy as np
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (round-to-nearest-even); return uint16 bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    bias = ((u >> np.uint64(16)) & np.uint64(1)) + np.uint64(0x7FFF)
-    out = ((u + bias) >> np.uint64(16)).astype(np.uint16)
+    u = a.view(np.uint32)
+    # u + 0x7FFF + lsb stays below 2^32 for every finite value and infinity
+    # (the largest, 0xFF7FFFFF, becomes 0xFF807FFF); NaNs are set afterwards.
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    out = ((u + bias) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
         out[nan] = np.uint16(0x7FC0)

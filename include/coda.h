@@ -15,17 +15,27 @@
  *    rounds its bf16 outputs to nearest-even.  Row/column statistics,
  *    losses and weight gradients are fp32.
  *  - All pointers are DEVICE pointers owned by the caller.  The library never
- *    allocates, frees or synchronises, and keeps no mutable global state;
- *    calls are asynchronous and ordered on `stream` (NULL = default stream).
+ *    allocates, frees or synchronises; calls are asynchronous and ordered on
+ *    `stream` (NULL = default stream).  Its only global state is a per-device
+ *    cache of two device properties (the gfx950 check and the compute-unit
+ *    count), each written once per device with atomic stores and safe to
+ *    read from any thread, and the environment switches below, read once.
  *  - Requirements: bf16 base pointers 16-byte aligned and bf16 ld % 8 == 0;
  *    fp32 matrix pointers 16-byte aligned and fp32 ld % 4 == 0; every output
- *    width (N, F, d, V) % 8 == 0; the reduction length K % 8 == 0 when the
- *    operand is contiguous along K (every forward and data-gradient call).
- *    The token count M is arbitrary; ragged edge tiles are masked.
+ *    width (N, F, d, V) % 8 == 0, except the SwiGLU activation width F
+ *    (coda_gemm_swiglu: F % 4 == 0 and ldact % 4 == 0); the reduction length
+ *    K % 8 == 0 when the operand is contiguous along K (every forward and
+ *    data-gradient call).  The token count M is arbitrary; ragged edge tiles
+ *    are masked.
  *  - Errors: validation happens before any launch and returns a status
  *    without touching the device.  CODA_ERR_HIP reports a launch error
  *    (hipGetLastError); device faults surface at the caller's next sync.
  *    Optional outputs ("opt") are skipped when NULL.
+ *  - Environment: CODA_LOG=1 prints each call's name and sizes to stderr.
+ *    CODA_DEBUG=1 checks, before any launch, that every matrix and vector
+ *    argument's byte extent ((rows - 1) * ld + cols elements) lies inside the
+ *    device allocation holding its base pointer, and returns CODA_ERR_BOUNDS
+ *    otherwise (coda_debug_extent is that check on its own).
  *  - Outputs must not alias inputs unless stated.  Results are deterministic:
  *    no atomics, fixed reduction order.
  */
@@ -49,7 +59,8 @@ typedef enum coda_status {
   CODA_ERR_ALIGN = 3,       /* a pointer or leading dimension is misaligned   */
   CODA_ERR_UNSUPPORTED = 4, /* device is not gfx950, or an untiled constraint */
   CODA_ERR_HIP = 5,         /* the HIP runtime reported an error              */
-  CODA_ERR_WORKSPACE = 6    /* workspace missing or too small                 */
+  CODA_ERR_WORKSPACE = 6,   /* workspace missing or too small                 */
+  CODA_ERR_BOUNDS = 7       /* CODA_DEBUG: an argument leaves its allocation  */
 } coda_status;
 
 /* Human-readable text of a status code (static storage). */
@@ -58,12 +69,22 @@ const char* coda_status_str(coda_status s);
 /* Library version string, e.g. "coda-gfx950 0.1". */
 const char* coda_version(void);
 
+/* CODA_DEBUG's extent check on its own: CODA_OK if [p, p + bytes) lies
+ * inside the device allocation that holds p (or p is NULL, or bytes is 0),
+ * CODA_ERR_BOUNDS otherwise.  Host-side query; launches nothing. */
+coda_status coda_debug_extent(const void* p, size_t bytes);
+
 /* Number of per-row partial columns a fused call writes for an output of
- * width N (one per 128-wide wavefront output tile): ceil(N / 128). */
+ * width N (one per 128-wide wavefront output tile): ceil(N / 128).  These
+ * are per-tile row reductions, the fourth epilogue primitive class of the
+ * reading notes "CODA GEMM-Epilogue Programming" (section 1), and the first
+ * level of the paper's two-level RMSNorm reduction (Figure 4). */
 int coda_nparts(int N);
 
 /* Number of per-column partial rows written by coda_gemm_rowscale_bwd for M
- * tokens (one per 128-token wavefront output tile): ceil(M / 128). */
+ * tokens (one per 128-token wavefront output tile): ceil(M / 128).  The
+ * per-tile column reductions of the same primitive class (reading notes
+ * section 1, class 4), used for dgamma. */
 int coda_mparts(int M);
 
 /* Tile plan of a fused GEMM with F output features (N, F or V of the call)
@@ -76,15 +97,21 @@ int coda_mparts(int M);
  * on twice as many compute units.  Both apply to coda_gemm, the forward
  * calls, coda_gemm_swiglu_bwd, coda_gemm_res_sumsq_bwd (dX) and the GEMMs
  * of the LM head; coda_gemm_rowscale_bwd and the weight gradients always use
- * 256 x 256 tiles.  Host-only: touches no device. */
+ * 256 x 256 tiles.  This plans the fixed mainloop that every call shares
+ * (paper abstract and Figure 3: the mainloop stays as it is and only the
+ * epilogue changes).  Host-only: touches no device. */
 int coda_tile_split(int F, int T, int cus);
 
-/* Workspace bytes coda_lmhead_ce needs for M rows and vocabulary V. */
+/* Workspace bytes coda_lmhead_ce needs for M rows and vocabulary V: the
+ * per-tile max and sum-exp statistics and the gathered target logits that
+ * the epilogue writes and the auxiliary reduction combines (reading notes
+ * section 2, "Cross-entropy loss"). */
 size_t coda_lmhead_ce_workspace(int M, int V);
 
 /* Minimal workspace bytes coda_lmhead_ce_bwd needs (one 256-row chunk of
- * bf16 dlogits); a larger workspace processes more rows per chunk, up to
- * M * V * 2 bytes (no chunking). */
+ * bf16 dlogits of the recomputed logits, reading notes section 2,
+ * "Cross-entropy loss"); a larger workspace processes more rows per chunk,
+ * up to M * V * 2 bytes (no chunking). */
 size_t coda_lmhead_ce_bwd_workspace(int M, int V, int d);
 
 /* ---------------------------------------------------------------------------
@@ -201,18 +228,26 @@ coda_status coda_gemm_rowscale_bwd(const coda_bf16* dY, int ldd, const coda_bf16
                                    coda_bf16* dU, int lddu, coda_bf16* N2, int ldn, float* gpart,
                                    int M, int d, int N, hipStream_t stream);
 
-/* Column reduction of the dgamma partials: dgamma_j = sum_q gpart[q, j]. */
+/* Column reduction of the dgamma partials: dgamma_j = sum_q gpart[q, j]
+ * (the auxiliary step after the epilogue's per-tile column reductions,
+ * reading notes section 1, class 4; dgamma of the RMSNorm backward,
+ * section 3).  gpart fp32 [mparts x d], dgamma fp32 [d]. */
 coda_status coda_col_reduce(const float* gpart, int mparts, int d, float* dgamma,
                             hipStream_t stream);
 
 /* RoPE backward epilogue: same arguments as coda_gemm_rope; applies the
- * inverse rotation (ang -> -ang) after the optional row scale. */
+ * inverse rotation (ang -> -ang) after the optional row scale.  The
+ * rotation is orthogonal, so its derivative map is the inverse rotation,
+ * fused into the GEMM that produces the gradient of the rotated output
+ * (reading notes section 3, "Reverse Fusion"; paper Figure 7). */
 coda_status coda_gemm_rope_bwd(const coda_bf16* A, int lda, const coda_bf16* W, int ldw,
                                const float* r, const int32_t* pos, float theta, int head_dim,
                                int n_rope, coda_bf16* Y, int ldy, int M, int N, int K,
                                hipStream_t stream);
 
-/* Backward of u = X W + Z:
+/* Backward of u = X W + Z (reading notes section 3: the gradient of the
+ * GEMM input is dU W^T, and the residual's gradient path is added in the
+ * same GEMM's epilogue):
  *   dX = dU W^T (+ dRes)   (bf16, M x K)       W [K x N] used transposed
  *   dW = X^T dU            (fp32, opt, K x N)  */
 coda_status coda_gemm_res_sumsq_bwd(const coda_bf16* dU, int ldu, const coda_bf16* W, int ldw,
@@ -221,7 +256,9 @@ coda_status coda_gemm_res_sumsq_bwd(const coda_bf16* dU, int ldu, const coda_bf1
                                     int M, int N, int K, hipStream_t stream);
 
 /* Weight gradient: dW[K x N] = X^T dY (fp32); accumulate != 0 adds into dW.
- * X [M x K], dY [M x N]; M (the reduction) is arbitrary. */
+ * X [M x K], dY [M x N]; M (the reduction) is arbitrary.  The weight
+ * gradient of every GEMM of the block (reading notes section 3), on the same
+ * fixed mainloop with an fp32 store epilogue. */
 coda_status coda_gemm_wgrad(const coda_bf16* X, int ldx, const coda_bf16* dY, int ldd,
                             float* dW, int lddw, int M, int K, int N, int accumulate,
                             hipStream_t stream);

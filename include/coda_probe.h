@@ -1,0 +1,36 @@
+/*
+ * coda_probe.h - measurement support of libcoda.so: a kernel that keeps every
+ * compute unit's matrix cores busy with independent bf16 MFMAs and nothing
+ * else, so that a benchmark can state the shader clock and the dense bf16
+ * rate this device actually sustains under a matrix-core load.  The fused
+ * GEMM-epilogue kernels are judged against the published peak (256 compute
+ * units x 2.4 GHz x 4096 FLOP per clock); this probe gives the clock that
+ * peak assumes, as measured, beside it.  It is not part of the computation.
+ *
+ * Conventions are those of coda.h (caller-owned device pointers, no
+ * allocation or synchronisation, launch on `stream`, coda_status return).
+ */
+#ifndef CODA_PROBE_H_
+#define CODA_PROBE_H_
+
+#include "coda.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Launches `blocks` workgroups of four waves; each workgroup holds more than
+ * half of a compute unit's LDS, so at most one runs per compute unit.  Every
+ * wave issues iters x 8 independent v_mfma_f32_32x32x16_bf16 (8 accumulator
+ * chains), i.e. blocks * 4 * iters * 8 * 32768 FLOP in total.  Wave 0 of
+ * workgroup b writes, as unsigned 64-bit counts, out[2b] = s_memtime ticks
+ * (shader clock) and out[2b + 1] = s_memrealtime ticks (the constant
+ * reference clock) elapsed over its MFMA loop.  out: device, 2 * blocks
+ * entries.  Needs 1 <= blocks <= 65536, 1 <= iters <= 1000000. */
+coda_status coda_probe_mfma(int blocks, int iters, unsigned long long* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CODA_PROBE_H_ */

@@ -1,6 +1,6 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
-include/coda.h and include/coda_unfused.h declare, and rejects bad arguments
-before any device call."""
+the public headers (include/coda.h, coda_unfused.h, coda_probe.h) declare,
+and rejects bad arguments before any device call."""
 
 import ctypes
 import os
@@ -31,8 +31,9 @@ def test_exports_every_header_function(L):
 
 
 def test_status_strings(L):
-    for s in range(7):
-        assert coda.status_str(s)
+    for s in range(8):
+        assert coda.status_str(s) and coda.status_str(s) != "unknown status"
+    assert coda.status_str(8) == "unknown status"
     assert coda.status_str(0) == "ok"
     assert L.coda_version().decode().startswith("coda-gfx950")
 
@@ -192,3 +193,16 @@ def test_no_kernel_spills():
     assert split, "no tile-count split kernels"
     assert all(v["agprs"] == 256 for v in gemm.values())
     assert all(v["lds"] <= 160 * 1024 for v in res.values())
+
+
+def test_probe_validation(L):
+    out = A16
+    assert L.coda_probe_mfma(0, 10, out, None) == 2          # no workgroups
+    assert L.coda_probe_mfma(4, 0, out, None) == 2           # no iterations
+    assert L.coda_probe_mfma(4, 10, None, None) == 1         # NULL output
+
+
+def test_debug_extent_null_or_empty(L):
+    # a NULL pointer or an empty extent passes without a device query
+    assert L.coda_debug_extent(None, 1 << 20) == 0
+    assert L.coda_debug_extent(A16, 0) == 0

@@ -186,6 +186,28 @@ def test_swiglu_fwd(with_r):
     assert_close(f64(act), O.swiglu(t), "act")
 
 
+@pytest.mark.parametrize("with_pre", [True, False])
+def test_swiglu_fwd_half_chunk_width(with_pre):
+    """Activation width F % 8 == 4 with ldact % 8 == 4 (rows end on half a
+    16-byte chunk); act and pre in canary-padded strided buffers."""
+    M, K, F = 300, 192, 260
+    say(f"case: swiglu fwd half-chunk act width M={M} K={K} F={F} ldact={F + 4} pre={with_pre}")
+    A = S.normal_bf16(54, (M, K))
+    Wgu = S.normal_bf16(55, (K, 2 * F), std=K ** -0.5)
+    r = (0.5 + np.random.default_rng(56).random(M)).astype(np.float32)
+    act_full, act = padded(M, F, torch.bfloat16, pad_cols=8)
+    assert act.stride(0) % 8 == 4
+    pre_full, pre = padded(M, 2 * F, torch.bfloat16) if with_pre else (None, None)
+    C().coda_gemm_swiglu(dev(A), dev(Wgu), dev(r), Act=act, Pre=pre, want_pre=with_pre)
+    torch.cuda.synchronize()
+    t = O.row_scale(r, O.gemm(A.f64(), Wgu.f64()))
+    assert_close(f64(act), O.swiglu(t), "act")
+    assert canary_intact(act_full, M, F)
+    if with_pre:
+        assert_close(f64(pre), t, "pre")
+        assert canary_intact(pre_full, M, 2 * F)
+
+
 def test_swiglu_bwd_and_s():
     M, N, F, d = 600, 264, 520, 264
     say(f"case: swiglu bwd M={M} N={N} F={F}")
