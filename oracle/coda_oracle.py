@@ -24,13 +24,20 @@ the bfloat16 inputs the GPU also consumes).  Sources:
         unscaled D, per-column RMSNorm weight applied to a side output).
 * [RoF] RoFormer (Su et al.), cited by the paper for rotary embeddings:
         rotate each adjacent feature pair by pos * theta^(-2k/head_dim).
+* [LN]  the paper's review page: the referee report (major comment 1) asks
+        for LayerNorm gradients as an epilogue composition and the simulated
+        rebuttal (point 1) promises the LayerNorm backward pass with its
+        residual-gradient path.  LayerNorm itself is the textbook one (Ba et
+        al.): n = ((u - mean) / sqrt(var + eps)) * gamma + beta with the
+        biased row variance.
 
 Readings where the pages leave a step open (each also listed in the design
 notes): RMSNorm is r = (mean_j u_ij^2 + eps)^(-1/2) with gamma applied after
 normalisation; SwiGLU pairs are adjacent columns (gate even, up odd) with
 a = silu(gate) * up; RoPE rotates adjacent pairs inside each head of the
 first ``n_rope`` columns; the LM-head loss is the mean over all rows with no
-ignore index; a label outside [0, V) gives a NaN row loss.
+ignore index; a label outside [0, V) gives a NaN row loss.  LayerNorm uses
+the biased variance with eps inside the root, like the RMSNorm reading.
 
 Parity pins: every public function here is pinned by tests/test_oracle_pins.py
 against closed forms, brute force, library special cases, algebraic identities
@@ -299,6 +306,101 @@ def block_bwd(p, f=None):
     g["dWgu1"] = gemm(f["n2_1"].T, g["dpre1"])
     dn2_1 = gemm(g["dpre1"], _f(p["Wgu1"]).T)
     g["du1"], g["dgamma1"], g["s1"], _ = rmsnorm_bwd(dn2_1, f["u1"], p["gamma1"], eps, dres=g["du2"])
+    g["dx"] = gemm(g["du1"], _f(p["W0"]).T)
+    g["dW0"] = gemm(_f(p["x"]).T, g["du1"])
+    g["dz"] = g["du1"]
+    return g
+
+
+# --------------------------------------------------------------------------
+# LayerNorm variant  [LN]
+# --------------------------------------------------------------------------
+
+
+def layernorm(u, gamma, beta, eps: float):
+    """Canonical LayerNorm over each row: n = (r (u - mu)) * gamma + beta with
+    mu = mean_j u, r = (mean_j (u - mu)^2 + eps)^(-1/2).  Returns (n, mu, r)."""
+    u = _f(u)
+    mu = np.mean(u, axis=1)
+    cu = u - mu[:, None]
+    r = 1.0 / np.sqrt(np.mean(cu * cu, axis=1) + eps)
+    return (r[:, None] * cu) * _f(gamma)[None, :] + _f(beta)[None, :], mu, r
+
+
+def ln_norm_block_fwd(x, w0, z, gamma, beta, w1, eps: float):
+    """Canonical y = layernorm(x W0 + z) W1.  Returns (y, u, mu, r)."""
+    u = residual(x, w0, z)
+    n, mu, r = layernorm(u, gamma, beta, eps)
+    return gemm(n, w1), u, mu, r
+
+
+def layernorm_bwd(dn, u, gamma, eps: float, dres=None):
+    """Canonical LayerNorm backward of n = xhat * gamma + beta, xhat = r (u - mu),
+    given dn = dL/dn:
+
+    gn = dn * gamma;  du = dres + r (gn - mean_j gn - xhat mean_j(gn xhat))
+    dgamma_j = sum_i dn_ij xhat_ij;  dbeta_j = sum_i dn_ij
+    Also returns the two row statistics a_i = mean_j gn_ij and
+    s_i = mean_j gn_ij xhat_ij.  Returns (du, dgamma, dbeta, a, s).
+    """
+    dn = _f(dn)
+    u = _f(u)
+    gamma = _f(gamma)
+    mu = np.mean(u, axis=1)
+    centered = u - mu[:, None]
+    r = 1.0 / np.sqrt(np.mean(centered * centered, axis=1) + eps)
+    xhat = r[:, None] * centered
+    gn = dn * gamma[None, :]
+    a = np.mean(gn, axis=1)
+    s = np.mean(gn * xhat, axis=1)
+    du = r[:, None] * (gn - a[:, None] - xhat * s[:, None])
+    if dres is not None:
+        du = du + _f(dres)
+    dgamma = np.sum(dn * xhat, axis=0)
+    dbeta = np.sum(dn, axis=0)
+    return du, dgamma, dbeta, a, s
+
+
+def ln_block_fwd(p):
+    """block_fwd with LayerNorm (gamma_l, beta_l) in place of RMSNorm:
+    u1 = x W0 + z; pre_l = layernorm(u_l) Wgu_l; a_l = swiglu(pre_l);
+    u2 = a1 Wd1 + u1; out = a2 Wd2 + u2.  Returns a dict of every intermediate."""
+    eps = p["eps"]
+    u1 = residual(p["x"], p["W0"], p["z"])
+    n_1, mu1, r1 = layernorm(u1, p["gamma1"], p["beta1"], eps)
+    pre1 = gemm(n_1, p["Wgu1"])
+    a1 = swiglu(pre1)
+    u2 = u1 + gemm(a1, p["Wd1"])
+    n_2, mu2, r2 = layernorm(u2, p["gamma2"], p["beta2"], eps)
+    pre2 = gemm(n_2, p["Wgu2"])
+    a2 = swiglu(pre2)
+    out = u2 + gemm(a2, p["Wd2"])
+    return dict(u1=u1, mu1=mu1, r1=r1, n_1=n_1, pre1=pre1, a1=a1, u2=u2, mu2=mu2, r2=r2, n_2=n_2, pre2=pre2,
+                a2=a2, out=out)
+
+
+def ln_block_bwd(p, f=None):
+    """Canonical chain-rule backward of ln_block_fwd from dOut; returns every
+    gradient and each layer's row statistics a_l, s_l."""
+    if f is None:
+        f = ln_block_fwd(p)
+    eps = p["eps"]
+    dOut = _f(p["dOut"])
+    g = {}
+    g["dWd2"] = gemm(f["a2"].T, dOut)
+    da2 = gemm(dOut, _f(p["Wd2"]).T)
+    g["dpre2"] = swiglu_bwd(da2, f["pre2"])
+    g["dWgu2"] = gemm(f["n_2"].T, g["dpre2"])
+    dn_2 = gemm(g["dpre2"], _f(p["Wgu2"]).T)
+    g["du2"], g["dgamma2"], g["dbeta2"], g["a2"], g["s2"] = layernorm_bwd(dn_2, f["u2"], p["gamma2"], eps,
+                                                                          dres=dOut)
+    g["dWd1"] = gemm(f["a1"].T, g["du2"])
+    da1 = gemm(g["du2"], _f(p["Wd1"]).T)
+    g["dpre1"] = swiglu_bwd(da1, f["pre1"])
+    g["dWgu1"] = gemm(f["n_1"].T, g["dpre1"])
+    dn_1 = gemm(g["dpre1"], _f(p["Wgu1"]).T)
+    g["du1"], g["dgamma1"], g["dbeta1"], g["a1"], g["s1"] = layernorm_bwd(dn_1, f["u1"], p["gamma1"], eps,
+                                                                          dres=g["du2"])
     g["dx"] = gemm(g["du1"], _f(p["W0"]).T)
     g["dW0"] = gemm(_f(p["x"]).T, g["du1"])
     g["dz"] = g["du1"]

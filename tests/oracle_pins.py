@@ -10,7 +10,9 @@ operand) is caught by at least one pin.
 
 Sources: "CODA GEMM-Epilogue Programming" (reading notes) sections 2 and 3;
 "CODA: Rewriting Transformer Blocks as GEMM-Epilogue Programs", Figures 4,
-5 and 7; RoFormer for the rotary map.
+5 and 7, and its review page (referee report, major comment 1; simulated
+rebuttal, point 1: the LayerNorm backward as an epilogue composition);
+RoFormer for the rotary map; Ba et al. for LayerNorm.
 """
 
 from __future__ import annotations
@@ -405,6 +407,170 @@ def check_block_s_statistics(O):
     d = p["x"].shape[1]
     _close(g["s2"], np.sum(g["dpre2"] * f["pre2"], axis=1) / d, 1e-12, "s2")
     _close(g["s1"], np.sum(g["dpre1"] * f["pre1"], axis=1) / d, 1e-12, "s1")
+
+
+# ----------------------------------------------------------------------------
+# LayerNorm variant (the paper's review page: LayerNorm gradients as an
+# epilogue composition)
+# ----------------------------------------------------------------------------
+
+
+def check_layernorm_torch(O):
+    """Forward against torch's float64 layer_norm, backward against its autograd."""
+    import torch
+
+    M, d, eps = 4, 7, 1e-3
+    u = _rand(M, d, seed=50) * 2 + 0.7
+    g = 1 + 0.1 * _rand(d, seed=51)
+    b = 0.2 * _rand(d, seed=52)
+    dn = _rand(M, d, seed=53)
+    dres = _rand(M, d, seed=54)
+    ut = torch.tensor(u, requires_grad=True)
+    gt = torch.tensor(g, requires_grad=True)
+    bt = torch.tensor(b, requires_grad=True)
+    nt = torch.nn.functional.layer_norm(ut, (d,), gt, bt, eps)
+    n, mu, r = O.layernorm(u, g, b, eps)
+    _close(n, nt.detach().numpy(), 1e-13, "layernorm vs torch")
+    (nt * torch.tensor(dn)).sum().backward()
+    du, dg, db, a, s = O.layernorm_bwd(dn, u, g, eps, dres=dres)
+    _close(du, ut.grad.numpy() + dres, 1e-12, "layernorm du vs torch autograd")
+    _close(dg, gt.grad.numpy(), 1e-12, "layernorm dgamma vs torch autograd")
+    _close(db, bt.grad.numpy(), 1e-12, "layernorm dbeta vs torch autograd")
+
+
+def check_layernorm_bruteforce(O):
+    """mean, variance, r and n of each row with exactly rounded sums."""
+    M, d, eps = 3, 6, 1e-2
+    u = _rand(M, d, seed=55) + 1.5
+    g = 1 + 0.1 * _rand(d, seed=56)
+    b = 0.3 * _rand(d, seed=57)
+    n, mu, r = O.layernorm(u, g, b, eps)
+    for i in range(M):
+        m = math.fsum(u[i]) / d
+        v = math.fsum((x - m) ** 2 for x in u[i]) / d
+        ri = 1.0 / math.sqrt(v + eps)
+        assert abs(mu[i] - m) < 1e-14 and abs(r[i] - ri) < 1e-13, ("layernorm stats", i)
+        for j in range(d):
+            assert abs(n[i, j] - ((u[i, j] - m) * ri * g[j] + b[j])) < 1e-13, ("layernorm", i, j)
+
+
+def check_layernorm_special_cases(O):
+    """Zero-mean rows with beta = 0 give RMSNorm; constant rows give beta;
+    a per-row shift changes nothing; the input gradient sums to 0 over a row
+    (apart from the residual path)."""
+    M, d, eps = 4, 8, 1e-6
+    u = _rand(M, d, seed=58)
+    u0 = u - u.mean(axis=1, keepdims=True)
+    g = 1 + 0.1 * _rand(d, seed=59)
+    b = 0.5 * _rand(d, seed=60)
+    _close(O.layernorm(u0, g, np.zeros(d), eps)[0], O.rmsnorm(u0, g, eps)[0], 1e-13, "zero-mean rows = RMSNorm")
+    const = np.repeat(np.array([[3.0], [-2.0], [0.0], [7.5]]), d, axis=1)
+    _close(O.layernorm(const, g, b, eps)[0], np.broadcast_to(b, (M, d)), 1e-15, "constant rows -> beta")
+    shift = _rand(M, 1, seed=61) * 5
+    _close(O.layernorm(u + shift, g, b, eps)[0], O.layernorm(u, g, b, eps)[0], 1e-12, "row shift invariance")
+    du, _, _, _, _ = O.layernorm_bwd(_rand(M, d, seed=62), u, g, eps)
+    _close(du.sum(axis=1), np.zeros(M), 1e-12, "du rows sum to 0")
+
+
+def check_ln_mean_corrected_commutation(O):
+    """layernorm(u) W1 = r (h3 - mu (gamma^T W1)) + beta^T W1 with h3 = (u * gamma) W1:
+    the row scale and the mean correction both move past the projection."""
+    M, K, d, N, eps = 5, 6, 8, 7, 1e-6
+    x = _rand(M, K, seed=63)
+    w0 = _rand(K, d, seed=64)
+    z = _rand(M, d, seed=65) + 0.8
+    g = 1 + 0.1 * _rand(d, seed=66)
+    b = 0.3 * _rand(d, seed=67)
+    w1 = _rand(d, N, seed=68)
+    y, u, mu, r = O.ln_norm_block_fwd(x, w0, z, g, b, w1, eps)
+    h3 = O.gemm(u * g[None, :], w1)
+    cvec = O.gemm(g[None, :], w1)[0]
+    bvec = O.gemm(b[None, :], w1)[0]
+    _close(r[:, None] * (h3 - mu[:, None] * cvec[None, :]) + bvec[None, :], y, 1e-12, "mean-corrected commutation")
+
+
+def check_layernorm_bwd_fd(O):
+    M, d, eps = 3, 6, 1e-3
+    u = _rand(M, d, seed=69) + 0.4
+    g = 1 + 0.1 * _rand(d, seed=70)
+    b = 0.2 * _rand(d, seed=71)
+    dn = _rand(M, d, seed=72)
+    dres = _rand(M, d, seed=73)
+    du, dg, db, _, _ = O.layernorm_bwd(dn, u, g, eps, dres=dres)
+    fu = lambda uu: float(np.sum(dn * O.layernorm(uu, g, b, eps)[0]) + np.sum(dres * uu))
+    fg = lambda gg: float(np.sum(dn * O.layernorm(u, gg, b, eps)[0]))
+    fb = lambda bb: float(np.sum(dn * O.layernorm(u, g, bb, eps)[0]))
+    _close(du, _fd_grad(fu, u), 1e-7, "layernorm du vs fd")
+    _close(dg, _fd_grad(fg, g), 1e-7, "layernorm dgamma vs fd")
+    _close(db, _fd_grad(fb, b), 1e-7, "layernorm dbeta vs fd")
+
+
+def check_ln_delayed_statistics(O):
+    """With y = n W1 and G = dY W1^T, the two row statistics come from the
+    next GEMM's output side: a = (1/d) dY (gamma^T W1)^T and
+    s = (1/d) (sumcols(dY * y) - dY (beta^T W1)^T); the delayed
+    du = dres + r (G * gamma) - r a - r^2 s (u - mu) is the canonical one;
+    dgamma = sum_i r G (u - mu), dbeta = sum_i G."""
+    M, d, N, eps = 4, 8, 5, 1e-6
+    u = _rand(M, d, seed=74) + 0.6
+    g = 1 + 0.1 * _rand(d, seed=75)
+    b = 0.3 * _rand(d, seed=76)
+    w1 = _rand(d, N, seed=77)
+    dY = _rand(M, N, seed=78)
+    dres = _rand(M, d, seed=79)
+    n, mu, r = O.layernorm(u, g, b, eps)
+    y = O.gemm(n, w1)
+    G = O.gemm(dY, w1.T)
+    du, dg, db, a, s = O.layernorm_bwd(G, u, g, eps, dres=dres)
+    cvec = O.gemm(g[None, :], w1)[0]
+    bvec = O.gemm(b[None, :], w1)[0]
+    _close(a, O.gemm(dY, cvec[:, None])[:, 0] / d, 1e-12, "a from dY and gamma^T W1")
+    _close(s, (np.sum(dY * y, axis=1) - O.gemm(dY, bvec[:, None])[:, 0]) / d, 1e-12, "s from dY, y and beta^T W1")
+    c = u - mu[:, None]
+    delayed = dres + r[:, None] * (G * g[None, :]) - (r * a)[:, None] - (r ** 2 * s)[:, None] * c
+    _close(delayed, du, 1e-12, "delayed LayerNorm backward")
+    _close(np.sum(r[:, None] * G * c, axis=0), dg, 1e-12, "dgamma from r G (u - mu)")
+    _close(np.sum(G, axis=0), db, 1e-12, "dbeta from G")
+
+
+def tiny_ln_block(seed=46, M=3, d=4, F=3):
+    p = tiny_block(seed=seed, M=M, d=d, F=F)
+    rng = np.random.default_rng(seed + 1000)
+    p["beta1"] = 0.3 * rng.standard_normal(d)
+    p["beta2"] = 0.3 * rng.standard_normal(d)
+    p["z"] = p["z"] + 0.5
+    return p
+
+
+def check_ln_block_bwd_fd(O):
+    p = tiny_ln_block()
+    g = O.ln_block_bwd(p)
+
+    def L(name):
+        def f(v):
+            q = dict(p)
+            q[name] = v
+            return float(np.sum(p["dOut"] * O.ln_block_fwd(q)["out"]))
+        return f
+
+    for name, gname in [("x", "dx"), ("z", "dz"), ("W0", "dW0"), ("gamma1", "dgamma1"), ("beta1", "dbeta1"),
+                        ("Wgu1", "dWgu1"), ("Wd1", "dWd1"), ("gamma2", "dgamma2"), ("beta2", "dbeta2"),
+                        ("Wgu2", "dWgu2"), ("Wd2", "dWd2")]:
+        _close(g[gname], _fd_grad(L(name), p[name]), 2e-7, f"LayerNorm block {gname}")
+
+
+def check_ln_block_statistics(O):
+    """Each layer's a_l and s_l from its SwiGLU backward's dpre_l and pre_l."""
+    p = tiny_ln_block(seed=47)
+    f = O.ln_block_fwd(p)
+    g = O.ln_block_bwd(p, f)
+    d = p["x"].shape[1]
+    for l in (1, 2):
+        cvec = O.gemm(p[f"gamma{l}"][None, :], p[f"Wgu{l}"])[0]
+        bvec = O.gemm(p[f"beta{l}"][None, :], p[f"Wgu{l}"])[0]
+        dpre, pre = g[f"dpre{l}"], f[f"pre{l}"]
+        _close(g[f"a{l}"], O.gemm(dpre, cvec[:, None])[:, 0] / d, 1e-12, f"a{l}")
+        _close(g[f"s{l}"], (np.sum(dpre * pre, axis=1) - O.gemm(dpre, bvec[:, None])[:, 0]) / d, 1e-12, f"s{l}")
 
 
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

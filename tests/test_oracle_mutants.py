@@ -42,6 +42,26 @@ MUTANTS = [
     ("block_bwd_skip_grad", "eps, dres=g[\"du2\"])", "eps, dres=dOut)"),
     ("block_bwd_wgrad_operand", "g[\"dWgu2\"] = gemm(f[\"n2_2\"].T, g[\"dpre2\"])", "g[\"dWgu2\"] = gemm(f[\"u2\"].T, g[\"dpre2\"])"),
     ("mlp_bwd_no_residual", "dX = gemm(dpre, _f(wgu).T) + dY", "dX = gemm(dpre, _f(wgu).T)"),
+    ("ln_no_centering", "cu = u - mu[:, None]", "cu = u"),
+    ("ln_unbiased_var", "r = 1.0 / np.sqrt(np.mean(cu * cu, axis=1) + eps)",
+     "r = 1.0 / np.sqrt(np.sum(cu * cu, axis=1) / (u.shape[1] - 1) + eps)"),
+    ("ln_eps_outside_sqrt", "r = 1.0 / np.sqrt(np.mean(cu * cu, axis=1) + eps)",
+     "r = 1.0 / (np.sqrt(np.mean(cu * cu, axis=1)) + eps)"),
+    ("ln_no_beta", "* _f(gamma)[None, :] + _f(beta)[None, :], mu, r", "* _f(gamma)[None, :], mu, r"),
+    ("ln_beta_before_gamma", "return (r[:, None] * cu) * _f(gamma)[None, :] + _f(beta)[None, :], mu, r",
+     "return (r[:, None] * cu + _f(beta)[None, :]) * _f(gamma)[None, :], mu, r"),
+    ("ln_bwd_no_mean_term", "du = r[:, None] * (gn - a[:, None] - xhat * s[:, None])",
+     "du = r[:, None] * (gn - xhat * s[:, None])"),
+    ("ln_bwd_no_s_term", "du = r[:, None] * (gn - a[:, None] - xhat * s[:, None])",
+     "du = r[:, None] * (gn - a[:, None])"),
+    ("ln_bwd_uncentered", "centered = u - mu[:, None]", "centered = u"),
+    ("ln_bwd_dgamma_no_r", "dgamma = np.sum(dn * xhat, axis=0)", "dgamma = np.sum(dn * centered, axis=0)"),
+    ("ln_bwd_dbeta_gamma", "dbeta = np.sum(dn, axis=0)", "dbeta = np.sum(dn * gamma[None, :], axis=0)"),
+    ("ln_block_wgrad_operand", "g[\"dWgu1\"] = gemm(f[\"n_1\"].T, g[\"dpre1\"])",
+     "g[\"dWgu1\"] = gemm(f[\"u1\"].T, g[\"dpre1\"])"),
+    ("ln_block_fwd_no_residual", "u2 = u1 + gemm(a1, p[\"Wd1\"])", "u2 = gemm(a1, p[\"Wd1\"])"),
+    ("ln_block_fwd_no_beta2", "layernorm(u2, p[\"gamma2\"], p[\"beta2\"], eps)",
+     "layernorm(u2, p[\"gamma2\"], 0.0 * p[\"beta2\"], eps)"),
 ]
 
 
