@@ -54,6 +54,8 @@ _SIGS = {
     "coda_gemm_wgrad": (I, [P, I, P, I, P, I, I, I, I, I, P]),
     "coda_lmhead_ce_bwd": (I, [P, I, P, I, P, P, F, P, I, P, I, P, SZ, I, I, I, P]),
     "coda_lmhead_ce_logits": (I, [P, I, P, I, P, P, P, P, P, I, P, SZ, I, I, I, P]),
+    "coda_lmhead_ce_noalloc": (I, [P, I, P, I, P, P, P, P, I, I, I, P]),
+    "coda_lmhead_ce_noalloc_max_bytes": (SZ, []),
     "coda_lmhead_ce_bwd_logits": (I, [P, I, P, I, P, P, F, P, I, P, I, P, I, I, I, I, P]),
     # include/coda_unfused.h
     "coda_unfused_add": (I, [P, I, P, I, P, I, I, I, P]),
@@ -267,6 +269,16 @@ def coda_lmhead_ce(H, W, labels, lse=None, loss_row=None, loss_mean=None, ws=Non
         ws = _empty((max(coda_lmhead_ce_workspace(M, V), 16),), torch.uint8, H)
     _call("coda_lmhead_ce", _ptr(H), _ld(H), _ptr(W), _ld(W), _ptr(labels), _ptr(lse), _ptr(loss_row),
           _ptr(loss_mean), _ptr(ws), ws.numel() * ws.element_size(), M, V, d, _stream())
+    return lse, loss_row, loss_mean
+
+
+def coda_lmhead_ce_noalloc(H, W, labels, lse, loss_row=None, loss_mean=None):
+    """coda_lmhead_ce with its workspace in the library's own device array;
+    the caller passes the outputs (loss_row / loss_mean may be None)."""
+    M, d = H.shape
+    V = W.shape[1]
+    _call("coda_lmhead_ce_noalloc", _ptr(H), _ld(H), _ptr(W), _ld(W), _ptr(labels), _ptr(lse), _ptr(loss_row),
+          _ptr(loss_mean), M, V, d, _stream())
     return lse, loss_row, loss_mean
 
 

@@ -5,6 +5,7 @@
 // the caller's stream and returns; nothing is allocated or synchronised.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -16,7 +17,36 @@ using namespace coda;
 using namespace coda_host;
 using namespace coda_launch;
 
+// The allocation-free LM-head statistics call (coda_lmhead_ce_noalloc) keeps
+// its partials workspace in this array: 64 MiB per device (one copy per GPU
+// the library runs on, held until the process ends), enough for the
+// coda_lmhead_ce workspace of M = 8192 tokens at a 128256-entry vocabulary
+// (65.8 MB).  Host code never passes the array's name to a kernel: it uses the
+// device address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device (each GPU holds its own copy at its own address).
+std::atomic<void*> g_scratch[64];
+
+coda_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CODA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return CODA_ERR_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return CODA_ERR_HIP;
+    }
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return CODA_OK;
+}
 
 // Merge of per-tile (max, sum exp) into lse and the row loss (reading notes
 // section 2, "Cross-entropy loss").  Partials are part-major ([nparts x ldp]).
@@ -127,7 +157,7 @@ static coda_status lmhead_ce_common(const coda_bf16* H, int ldh, const coda_bf16
                                     const int32_t* labels, float* lse, float* loss_row,
                                     float* loss_mean, coda_bf16* logits, int ldl, bool keep,
                                     void* ws, size_t ws_bytes, int M, int V, int d,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, bool use_scratch = false) {
   Check c;
   c.shape(M >= 0 && V >= 0 && d >= 0);
   c.bmat(H, ldh, d, M);
@@ -140,9 +170,16 @@ static coda_status lmhead_ce_common(const coda_bf16* H, int ldh, const coda_bf16
   c.shape(V % 8 == 0 && d % 8 == 0);
   if (c.st != CODA_OK) return c.st;
   if (M == 0 || V == 0) return CODA_OK;
-  if (ws == nullptr || !al16(ws) || ws_bytes < coda_lmhead_ce_workspace(M, V))
-    return CODA_ERR_WORKSPACE;
-  if (coda_status s = c.device()) return s;
+  if (use_scratch) {
+    if (coda_lmhead_ce_workspace(M, V) > kScratchBytes) return CODA_ERR_WORKSPACE;
+    if (coda_status s = c.device()) return s;
+    if (coda_status s = scratch_address(&ws)) return s;
+    ws_bytes = kScratchBytes;
+  } else {
+    if (ws == nullptr || !al16(ws) || ws_bytes < coda_lmhead_ce_workspace(M, V))
+      return CODA_ERR_WORKSPACE;
+    if (coda_status s = c.device()) return s;
+  }
   const int np = coda_nparts(V);
   float* pm = static_cast<float*>(ws);
   float* ps = pm + (size_t)M * np;
@@ -172,6 +209,18 @@ coda_status coda_lmhead_ce(const coda_bf16* H, int ldh, const coda_bf16* W, int 
   trace("coda_lmhead_ce", "M=%d V=%d d=%d ws_bytes=%zu", M, V, d, ws_bytes);
   return lmhead_ce_common(H, ldh, W, ldw, labels, lse, loss_row, loss_mean, nullptr, 0, false, ws,
                           ws_bytes, M, V, d, stream);
+}
+
+size_t coda_lmhead_ce_noalloc_max_bytes(void) { return kScratchBytes; }
+
+coda_status coda_lmhead_ce_noalloc(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
+                                   const int32_t* labels, float* lse, float* loss_row, float* loss_mean,
+                                   int M, int V, int d, hipStream_t stream) {
+  trace("coda_lmhead_ce_noalloc", "M=%d V=%d d=%d", M, V, d);
+  // Every partial, target and row-loss entry the merge kernel reads is written
+  // earlier in the same call, so the array needs no clearing between calls.
+  return lmhead_ce_common(H, ldh, W, ldw, labels, lse, loss_row, loss_mean, nullptr, 0, false, nullptr, 0,
+                          M, V, d, stream, true);
 }
 
 coda_status coda_lmhead_ce_logits(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,

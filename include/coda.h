@@ -185,6 +185,24 @@ coda_status coda_lmhead_ce(const coda_bf16* H, int ldh, const coda_bf16* W, int 
                            const int32_t* labels, float* lse, float* loss_row, float* loss_mean,
                            void* ws, size_t ws_bytes, int M, int V, int d, hipStream_t stream);
 
+/* coda_lmhead_ce for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and arguments without the workspace.  The partials
+ * live in a 64 MiB array that the library holds in device memory, one per
+ * GPU, from the first call on that device until the process ends
+ * (coda_lmhead_ce_noalloc_max_bytes() returns its size); a call whose
+ * coda_lmhead_ce_workspace(M, V) exceeds it returns CODA_ERR_WORKSPACE.
+ * It calls no allocation routine.  Every call on one GPU shares that array:
+ * calls that overlap on one GPU (other streams, other threads) race and give
+ * wrong results; calls ordered on one stream are safe (each writes every
+ * entry it reads). */
+coda_status coda_lmhead_ce_noalloc(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
+                                   const int32_t* labels, float* lse, float* loss_row,
+                                   float* loss_mean, int M, int V, int d, hipStream_t stream);
+
+/* Size in bytes of the array coda_lmhead_ce_noalloc uses (67108864). */
+size_t coda_lmhead_ce_noalloc_max_bytes(void);
+
 /* coda_lmhead_ce that also keeps the logits: the same statistics, taken from
  * the fp32 logits, plus logits (bf16, M x V, leading dimension ldl, required)
  * written by the same epilogue.  For coda_lmhead_ce_bwd_logits, which then

@@ -206,3 +206,16 @@ def test_debug_extent_null_or_empty(L):
     # a NULL pointer or an empty extent passes without a device query
     assert L.coda_debug_extent(None, 1 << 20) == 0
     assert L.coda_debug_extent(A16, 0) == 0
+
+
+def test_noalloc_limits(L):
+    """coda_lmhead_ce_noalloc: the array covers the full LM-head workload;
+    a larger need or a bad argument is refused before any device call."""
+    assert L.coda_lmhead_ce_noalloc_max_bytes() == 64 << 20
+    assert coda.coda_lmhead_ce_workspace(8192, 128256) <= L.coda_lmhead_ce_noalloc_max_bytes()
+    # V = 200000 at M = 8192 needs (2 * 8192 * 1563 + 2 * 8192) * 4 bytes = 102 MB
+    assert L.coda_lmhead_ce_noalloc(A16, 64, A16b, 200000, A16c, A16, None, None, 8192, 200000, 64, None) == 6
+    assert L.coda_lmhead_ce_noalloc(None, 64, A16b, 128, A16c, A16, None, None, 16, 128, 64, None) == 1
+    assert L.coda_lmhead_ce_noalloc(A16, 64, A16b, 128, A16c, A16, None, None, 16, 124, 64, None) == 2
+    # no rows: nothing to do
+    assert L.coda_lmhead_ce_noalloc(A16, 64, A16b, 128, A16c, A16, None, None, 0, 128, 64, None) == 0
