@@ -31,7 +31,7 @@ RESOURCES = os.path.join(HERE, "libcoda.resources.json")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["coda_aux.hip", "coda_fwd.hip", "coda_pair.hip", "coda_bwd.hip", "coda_ce.hip", "coda_unfused.hip",
-           "coda_probe.hip"]
+           "coda_probe.hip", "coda_ln.hip"]
 OBJDIR = os.path.join(HERE, "_build")
 
 FLAGS = [

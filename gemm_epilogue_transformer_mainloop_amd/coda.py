@@ -57,6 +57,15 @@ _SIGS = {
     "coda_lmhead_ce_noalloc": (I, [P, I, P, I, P, P, P, P, I, I, I, P]),
     "coda_lmhead_ce_noalloc_max_bytes": (SZ, []),
     "coda_lmhead_ce_bwd_logits": (I, [P, I, P, I, P, P, F, P, I, P, I, P, I, I, I, I, P]),
+    # LayerNorm variant
+    "coda_gemm_res_lnstats": (I, [P, I, P, I, P, I, P, P, I, P, I, P, P, I, I, I, P]),
+    "coda_row_ln": (I, [P, P, I, I, I, F, P, P, P]),
+    "coda_ln_colvec": (I, [P, I, P, P, I, I, P, P, P]),
+    "coda_gemm_ln_rowscale": (I, [P, I, P, I, P, P, P, P, P, I, I, I, I, P]),
+    "coda_gemm_ln_swiglu": (I, [P, I, P, I, P, P, P, P, P, I, P, I, I, I, I, P]),
+    "coda_gemm_swiglu_bwd_ln": (I, [P, I, P, I, P, I, P, I, P, P, P, P, I, I, I, P]),
+    "coda_row_ln_bwd": (I, [P, P, I, I, I, P, P, P]),
+    "coda_gemm_ln_bwd": (I, [P, I, P, I, P, I, P, P, P, P, P, P, P, I, P, I, P, I, P, P, I, I, I, P]),
     # include/coda_unfused.h
     "coda_unfused_add": (I, [P, I, P, I, P, I, I, I, P]),
     "coda_unfused_add_rmsnorm": (I, [P, I, P, I, P, F, P, I, P, I, P, I, I, P]),
@@ -403,6 +412,116 @@ def coda_lmhead_ce_bwd_logits(H, W, labels, lse, grad_scale: float, logits, dH=N
           ctypes.c_float(grad_scale), _ptr(logits), _ld(logits), _ptr(dH), _ld(dH), _ptr(dW), _ld(dW),
           M, V, d, _stream())
     return dH, dW
+
+
+# ----------------------------------------------------------------------------
+# LayerNorm variant
+# ----------------------------------------------------------------------------
+
+
+def coda_gemm_res_lnstats(X, W, Z=None, gamma=None, U=None, H2=None, pmean=None, pm2=None, want_h2=True):
+    M, K = X.shape
+    N = W.shape[1]
+    if U is None:
+        U = _empty((M, N), torch.bfloat16, X)
+    if H2 is None and want_h2 and gamma is not None:
+        H2 = _empty((M, N), torch.bfloat16, X)
+    if pmean is None:
+        pmean = _empty((M, coda_nparts(N)), torch.float32, X)
+    if pm2 is None:
+        pm2 = _empty((M, coda_nparts(N)), torch.float32, X)
+    _dense(pmean, "pmean"), _dense(pm2, "pm2")
+    _call("coda_gemm_res_lnstats", _ptr(X), _ld(X), _ptr(W), _ld(W), _ptr(Z), _ld(Z), _ptr(gamma), _ptr(U), _ld(U),
+          _ptr(H2), _ld(H2), _ptr(pmean), _ptr(pm2), M, N, K, _stream())
+    return U, H2, pmean, pm2
+
+
+def coda_row_ln(pmean, pm2, d: int, eps: float, mu=None, r=None):
+    _dense(pmean, "pmean"), _dense(pm2, "pm2")
+    M, np_ = pmean.shape
+    if mu is None:
+        mu = _empty((M,), torch.float32, pmean)
+    if r is None:
+        r = _empty((M,), torch.float32, pmean)
+    _call("coda_row_ln", _ptr(pmean), _ptr(pm2), np_, M, d, ctypes.c_float(eps), _ptr(mu), _ptr(r), _stream())
+    return mu, r
+
+
+def coda_ln_colvec(W, gamma, beta=None, cvec=None, bvec=None):
+    K, N = W.shape
+    if cvec is None:
+        cvec = _empty((N,), torch.float32, W)
+    if bvec is None and beta is not None:
+        bvec = _empty((N,), torch.float32, W)
+    _call("coda_ln_colvec", _ptr(W), _ld(W), _ptr(gamma), _ptr(beta), K, N, _ptr(cvec), _ptr(bvec), _stream())
+    return cvec, bvec
+
+
+def coda_gemm_ln_rowscale(A, W, r, mu, cvec, bvec=None, Y=None):
+    M, K = A.shape
+    N = W.shape[1]
+    if Y is None:
+        Y = _empty((M, N), torch.bfloat16, A)
+    _call("coda_gemm_ln_rowscale", _ptr(A), _ld(A), _ptr(W), _ld(W), _ptr(r), _ptr(mu), _ptr(cvec), _ptr(bvec),
+          _ptr(Y), _ld(Y), M, N, K, _stream())
+    return Y
+
+
+def coda_gemm_ln_swiglu(A, Wgu, r, mu, cvec, bvec=None, Act=None, Pre=None, want_pre=True):
+    M, K = A.shape
+    F = Wgu.shape[1] // 2
+    if Act is None:
+        Act = _empty((M, F), torch.bfloat16, A)
+    if Pre is None and want_pre:
+        Pre = _empty((M, 2 * F), torch.bfloat16, A)
+    _call("coda_gemm_ln_swiglu", _ptr(A), _ld(A), _ptr(Wgu), _ld(Wgu), _ptr(r), _ptr(mu), _ptr(cvec), _ptr(bvec),
+          _ptr(Act), _ld(Act), _ptr(Pre), _ld(Pre), M, F, K, _stream())
+    return Act, Pre
+
+
+def coda_gemm_swiglu_bwd_ln(dOut, Wd, Pre, cvec, bvec=None, dPre=None, spart=None, apart=None):
+    M, N = dOut.shape
+    F = Wd.shape[0]
+    if dPre is None:
+        dPre = _empty((M, 2 * F), torch.bfloat16, dOut)
+    if spart is None:
+        spart = _empty((M, coda_nparts(F)), torch.float32, dOut)
+    if apart is None:
+        apart = _empty((M, coda_nparts(F)), torch.float32, dOut)
+    _dense(spart, "spart"), _dense(apart, "apart")
+    _call("coda_gemm_swiglu_bwd_ln", _ptr(dOut), _ld(dOut), _ptr(Wd), _ld(Wd), _ptr(Pre), _ld(Pre), _ptr(dPre),
+          _ld(dPre), _ptr(cvec), _ptr(bvec), _ptr(spart), _ptr(apart), M, F, N, _stream())
+    return dPre, spart, apart
+
+
+def coda_row_ln_bwd(spart, apart, d: int, s=None, a=None):
+    _dense(spart, "spart"), _dense(apart, "apart")
+    M, np_ = spart.shape
+    if s is None:
+        s = _empty((M,), torch.float32, spart)
+    if a is None:
+        a = _empty((M,), torch.float32, spart)
+    _call("coda_row_ln_bwd", _ptr(spart), _ptr(apart), np_, M, d, _ptr(s), _ptr(a), _stream())
+    return s, a
+
+
+def coda_gemm_ln_bwd(dY, W1, U, gamma, beta, r, mu, s, a, dRes=None, dU=None, N2=None, gpart=None, bgpart=None,
+                     want_n2=True):
+    M, N = dY.shape
+    d = W1.shape[0]
+    if dU is None:
+        dU = _empty((M, d), torch.bfloat16, dY)
+    if N2 is None and want_n2:
+        N2 = _empty((M, d), torch.bfloat16, dY)
+    if gpart is None:
+        gpart = _empty((coda_mparts(M), d), torch.float32, dY)
+    if bgpart is None:
+        bgpart = _empty((coda_mparts(M), d), torch.float32, dY)
+    _dense(gpart, "gpart"), _dense(bgpart, "bgpart")
+    _call("coda_gemm_ln_bwd", _ptr(dY), _ld(dY), _ptr(W1), _ld(W1), _ptr(U), _ld(U), _ptr(gamma), _ptr(beta),
+          _ptr(r), _ptr(mu), _ptr(s), _ptr(a), _ptr(dRes), _ld(dRes), _ptr(dU), _ld(dU), _ptr(N2), _ld(N2),
+          _ptr(gpart), _ptr(bgpart), M, d, N, _stream())
+    return dU, N2, gpart, bgpart
 
 
 # ----------------------------------------------------------------------------

@@ -82,6 +82,41 @@ __device__ __forceinline__ u32x4 vload16_bf16(const uint16_t* v, int i, int n) {
   return ld16(v + (i < n ? i : n - 8));
 }
 
+// Eight consecutive fp32 vector entries v[f .. f+7] (f clamped into range;
+// n % 8 == 0), or zeros when v is NULL (a uniform branch).
+__device__ __forceinline__ void load8f(const float* v, int f, int n, float (&o)[8]) {
+  if (v == nullptr) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+    return;
+  }
+  const float* p = v + (f < n ? f : n - 8);
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[e] = a[e];
+    o[4 + e] = b[e];
+  }
+}
+
+// Eight fp32 values from 32 bytes of LDS.
+__device__ __forceinline__ void unpack_f32x8(const char* p, float (&o)[8]) {
+  const f32x4 a = __builtin_bit_cast(f32x4, ld16(p)), b = __builtin_bit_cast(f32x4, ld16(p + 16));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[e] = a[e];
+    o[4 + e] = b[e];
+  }
+}
+
+// The LayerNorm form of GEMM2's delayed row transform (the mean-corrected
+// commutation of LayerNorm with the projection W): with h3 = (u * gamma) W
+// in the accumulator, y = r (h3 - mu c) + b, c = gamma^T W, b = beta^T W.
+__device__ __forceinline__ void ln_row(float (&v)[8], float r, float mu, const float (&c)[8], const float (&b)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = fmaf(r, fmaf(-mu, c[e], v[e]), b[e]);
+}
+
 // Eight accumulator elements of block (ri, ci), copied from their AGPRs at
 // this point of the program.  Left to itself the register allocator copies
 // all 256 accumulators into VGPRs where the main loop ends, which takes every
@@ -138,13 +173,18 @@ struct Stage {
 // Store-only / row-scale / residual epilogue:  Y = bf16( r_t * acc + res )
 // (plain GEMM; GEMM2's delayed RMSNorm scale; data-gradient + residual)
 // ---------------------------------------------------------------------------
-template <bool HAS_R, bool HAS_RES>
+// LN: the LayerNorm form of the delayed transform (ln_row), with per-token
+// mu and per-feature c = gamma^T W, b = beta^T W (b may be NULL).
+template <bool HAS_R, bool HAS_RES, bool LN = false>
 struct EpiLinear {
   const float* r;
   const uint16_t* res;
   int ldres;
   uint16_t* Y;
   int ldy;
+  const float* mu = nullptr;
+  const float* cvec = nullptr;
+  const float* bvec = nullptr;
 
   static constexpr int LDS_BYTES = STAGE_LDS;
 
@@ -166,25 +206,53 @@ struct EpiLinear {
 #pragma unroll
           for (int h = 0; h < 2; ++h) rv[ci][ri][h] = rz.load16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h));
     }
+    if constexpr (LN) {
+      // feature runs outer, so c and b are loaded once per run
+      float mus[CI];
 #pragma unroll
-    for (int ci = 0; ci < CI; ++ci) {
-      const float rs = rsv[ci];
+      for (int ci = 0; ci < CI; ++ci) mus[ci] = vload(mu, g.tw0 + L.t(ci), g.T);
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          float v[8];
-          acc8(acc, ri, ci, h, v);
+          float cv[8], bv[8];
+          load8f(cvec, g.fw0 + L.f(ri, h), g.F, cv);
+          load8f(bvec, g.fw0 + L.f(ri, h), g.F, bv);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] *= rs;
-          if constexpr (HAS_RES) {
-            float z[8];
-            unpack8(rv[ci][ri][h], z);
+          for (int ci = 0; ci < CI; ++ci) {
+            float v[8];
+            acc8(acc, ri, ci, h, v);
+            ln_row(v, rsv[ci], mus[ci], cv, bv);
+            if constexpr (HAS_RES) {
+              float z[8];
+              unpack8(rv[ci][ri][h], z);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] += z[e];
+              for (int e = 0; e < 8; ++e) v[e] += z[e];
+            }
+            stage.put(g, ci, ri, h, pack8(v));
           }
-          stage.put(g, ci, ri, h, pack8(v));
         }
+    } else {
+#pragma unroll
+      for (int ci = 0; ci < CI; ++ci) {
+        const float rs = rsv[ci];
+#pragma unroll
+        for (int ri = 0; ri < RI; ++ri)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float v[8];
+            acc8(acc, ri, ci, h, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] *= rs;
+            if constexpr (HAS_RES) {
+              float z[8];
+              unpack8(rv[ci][ri][h], z);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] += z[e];
+            }
+            stage.put(g, ci, ri, h, pack8(v));
+          }
+      }
     }
     stage.flush<CI, HAS_RES>(g, y);  // residual-stream outputs: non-temporal
   }
@@ -195,7 +263,11 @@ struct EpiLinear {
 // Listing 2): u = acc + z; U = bf16(u); H2 = bf16(u * gamma);
 // part[t, pf] = sum over the wave's features of u^2 (unscaled, fp32).
 // ---------------------------------------------------------------------------
-template <bool HAS_Z, bool HAS_H2, bool HAS_PART>
+// LN: instead of the sum of squares, the LayerNorm statistics of the wave
+// tile: part = the tile's mean of u, part2 = its sum of squared deviations
+// from that mean (runs of 8 features, each exact in two passes, merged with
+// the pairwise-update formula of Chan, Golub and LeVeque).
+template <bool HAS_Z, bool HAS_H2, bool HAS_PART, bool LN = false>
 struct EpiResSumsq {
   const uint16_t* z;
   int ldz;
@@ -206,6 +278,7 @@ struct EpiResSumsq {
   int ldh;
   float* part;
   int nparts;
+  float* part2 = nullptr;
 
   static constexpr int LDS_BYTES = STAGE_LDS;
 
@@ -247,6 +320,7 @@ struct EpiResSumsq {
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
       float ss = 0.0f;
+      float na = 0.0f, ma = 0.0f;  // LN: count and mean of the runs merged so far (M2 in ss)
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
@@ -255,10 +329,25 @@ struct EpiResSumsq {
           float v[8];
           u8(ci, ri, h, v);
           stage.put(g, ci, ri, h, pack8(v));
-          float sq = 0.0f;
+          if constexpr (LN) {
+            float sm = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sq += v[e] * v[e];
-          ss += ok ? sq : 0.0f;
+            for (int e = 0; e < 8; ++e) sm += v[e];
+            const float mb = sm * 0.125f;
+            float m2b = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m2b = fmaf(v[e] - mb, v[e] - mb, m2b);
+            const float nb = ok ? 8.0f : 0.0f, nn = na + nb;
+            const float w = nn > 0.0f ? nb / nn : 0.0f, dl = mb - ma;
+            ma = fmaf(dl, w, ma);
+            ss += (ok ? m2b : 0.0f) + dl * dl * na * w;
+            na = nn;
+          } else {
+            float sq = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sq += v[e] * v[e];
+            ss += ok ? sq : 0.0f;
+          }
           if constexpr (HAS_H2) {
             float gm[8], hv[8];
             unpack8(gv[ri][h], gm);
@@ -267,7 +356,19 @@ struct EpiResSumsq {
             ho.store16(L.t(ci), L.f(ri, h), ok, pack8(hv));
           }
         }
-      if constexpr (HAS_PART) {
+      if constexpr (LN) {
+        // merge with the other half of the token's 128 features (lane l ^ 32)
+        const float nb = __shfl_xor(na, 32), mb = __shfl_xor(ma, 32), m2b = __shfl_xor(ss, 32);
+        const float nn = na + nb;
+        const float w = nn > 0.0f ? nb / nn : 0.0f, dl = mb - ma;
+        const float mt = fmaf(dl, w, ma), m2t = ss + m2b + dl * dl * na * w;
+        const bool wr = g.hh == 0 && L.tok(ci) && L.F > 0;
+        const int t = g.tw0 + L.t(ci);
+        if (wr) {
+          part[(size_t)t * nparts + g.pf] = mt;
+          part2[(size_t)t * nparts + g.pf] = m2t;
+        }
+      } else if constexpr (HAS_PART) {
         ss = sum_halves(ss);
         const bool w = g.hh == 0 && L.tok(ci) && L.F > 0;
         const int t = g.tw0 + L.t(ci);
@@ -427,13 +528,18 @@ struct StageAct {
 // a_j = g sigmoid(g) v; optional Pre = bf16(g, v) for the backward pass.
 // The GEMM's feature space is the interleaved 2F columns.
 // ---------------------------------------------------------------------------
-template <bool HAS_R, bool HAS_PRE>
+// LN: the pre-activation is the LayerNorm form r (acc - mu c) + b (ln_row)
+// over the interleaved 2F columns, c = gamma^T Wgu, b = beta^T Wgu.
+template <bool HAS_R, bool HAS_PRE, bool LN = false>
 struct EpiSwiglu {
   const float* r;
   uint16_t* act;
   int ldact;
   uint16_t* pre;
   int ldp;
+  const float* mu = nullptr;
+  const float* cvec = nullptr;
+  const float* bvec = nullptr;
 
   // pre (when kept) and then act leave through the released LDS.
   static constexpr int LDS_BYTES = STAGE_LDS;
@@ -444,9 +550,12 @@ struct EpiSwiglu {
     const TileView<2> ao(act, ldact, g.tw0, g.fw0 >> 1);
     const TileView<2> po(pre, ldp, g.tw0, g.fw0);
     const StageAct sa(smem);
-    float rsv[CI];
+    float rsv[CI], mus[CI];
 #pragma unroll
-    for (int ci = 0; ci < CI; ++ci) rsv[ci] = HAS_R ? vload(r, g.tw0 + L.t(ci), g.T) : 1.0f;
+    for (int ci = 0; ci < CI; ++ci) {
+      rsv[ci] = HAS_R ? vload(r, g.tw0 + L.t(ci), g.T) : 1.0f;
+      mus[ci] = LN ? vload(mu, g.tw0 + L.t(ci), g.T) : 0.0f;
+    }
     u32x4 aout[CI][RI];
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
@@ -459,8 +568,15 @@ struct EpiSwiglu {
         for (int h = 0; h < 2; ++h) {
           float v[8];
           acc8(acc, ri, ci, h, v);
+          if constexpr (LN) {
+            float cv[8], bv[8];
+            load8f(cvec, g.fw0 + L.f(ri, h), g.F, cv);
+            load8f(bvec, g.fw0 + L.f(ri, h), g.F, bv);
+            ln_row(v, rs, mus[ci], cv, bv);
+          } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] *= rs;
+            for (int e = 0; e < 8; ++e) v[e] *= rs;
+          }
           float a[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -649,7 +765,11 @@ struct EpiCEBwd {
 // (g, v) = Pre[2j, 2j+1]; dPre = (da v s (1 + g (1 - s)), da g s);
 // spart[t, pf] = sum (dPre_2j g + dPre_2j+1 v)  (RMSNorm statistic partial).
 // ---------------------------------------------------------------------------
-template <bool HAS_SPART>
+// LN: the two LayerNorm row statistics of the layer whose output pre is
+// (the reading notes' "Eliminating the RMSNorm backward kernel", applied to
+// LayerNorm): spart = sum dpre (pre - b) and apart = sum dpre c over the
+// wave's columns, c = gamma^T Wgu, b = beta^T Wgu (b may be NULL).
+template <bool HAS_SPART, bool LN = false>
 struct EpiSwigluBwd {
   const uint16_t* pre;
   int ldp;
@@ -657,10 +777,14 @@ struct EpiSwigluBwd {
   int lddp;
   float* spart;
   int nparts;
+  const float* cvec = nullptr;
+  const float* bvec = nullptr;
+  float* apart = nullptr;
 
   // The epilogue stages pre and dpre through the LDS the main loop has
-  // released (32 KiB per wave, 128 KiB per workgroup).
-  static constexpr int LDS_BYTES = 4 * 32768;
+  // released (32 KiB per wave, 128 KiB per workgroup); LN adds 2 KiB per wave
+  // beyond them for the wave's 256 columns of c and b.
+  static constexpr int LDS_BYTES = 4 * 32768 + (LN ? 4 * 2048 : 0);
 
   // Each wave works on its (32 CI)-token x 256-column pre/dpre tile in CI
   // phases of 32 tokens (16 KiB), double-buffered in its 32 KiB LDS slice:
@@ -699,8 +823,23 @@ struct EpiSwigluBwd {
         dma16<true>(base, 0x7fffffffu, ok ? (uint32_t)(r * ldp + 8 * c) * 2u : OOB, buf + i * 1024);
       }
     };
-    fetch(0);
-    fetch(1);
+    [[maybe_unused]] char* cb = smem + 4 * 32768 + wave * 2048;  // LN: c at [0, 1 KiB), b after it
+    if constexpr (LN) {
+      // The wave's 256 pre columns of c and b, 4 per lane, loaded before the
+      // phase DMAs (so the wait below does not wait for those).
+      const int col = 2 * g.fw0 + 4 * g.lane;
+      const bool in = col < 2 * g.F;
+      const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4 cq = in ? *reinterpret_cast<const f32x4*>(cvec + col) : zero;
+      const f32x4 bq = (in && bvec) ? *reinterpret_cast<const f32x4*>(bvec + col) : zero;
+      fetch(0);
+      fetch(1);
+      st16(cb + 16 * g.lane, __builtin_bit_cast(u32x4, cq));
+      st16(cb + 1024 + 16 * g.lane, __builtin_bit_cast(u32x4, bq));
+    } else {
+      fetch(0);
+      fetch(1);
+    }
 #pragma unroll
     for (int p = 0; p < CI; ++p) {
       // Operations issued after phase p's DMA: p = 0: phase 1's DMA;
@@ -715,7 +854,7 @@ struct EpiSwigluBwd {
       // dpre from pre and da in the accumulator layout, in place.
       const int ci = p;
       const int r = g.lt;
-      float ss = 0.0f;
+      float ss = 0.0f, sa = 0.0f;
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
 #pragma unroll
@@ -729,7 +868,12 @@ struct EpiSwigluBwd {
             char* a = buf + r * 512 + ((chunk ^ (r & 7)) << 4);
             float pvv[8], out[8];
             unpack8(ld16(a), pvv);
-            float part = 0.0f;
+            float cv[8], bv[8];
+            if constexpr (LN) {
+              unpack_f32x8(cb + 32 * chunk, cv);
+              unpack_f32x8(cb + 1024 + 32 * chunk, bv);
+            }
+            float part = 0.0f, pa = 0.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const float da = dav[4 * c + q];
@@ -739,17 +883,27 @@ struct EpiSwigluBwd {
               const float du = da * gg * sg;
               out[2 * q] = dg;
               out[2 * q + 1] = du;
-              part += dg * gg + du * uu;
+              if constexpr (LN) {
+                part += dg * (gg - bv[2 * q]) + du * (uu - bv[2 * q + 1]);
+                pa += dg * cv[2 * q] + du * cv[2 * q + 1];
+              } else {
+                part += dg * gg + du * uu;
+              }
             }
             ss += ok ? part : 0.0f;
+            if constexpr (LN) sa += ok ? pa : 0.0f;
             st16(a, pack8(out));
           }
         }
       if constexpr (HAS_SPART) {
         ss = sum_halves(ss);
+        if constexpr (LN) sa = sum_halves(sa);
         const bool w = g.hh == 0 && L.tok(ci) && L.F > 0;
         const int t = g.tw0 + L.t(ci);
-        if (w) spart[(size_t)t * nparts + g.pf] = ss;
+        if (w) {
+          spart[(size_t)t * nparts + g.pf] = ss;
+          if constexpr (LN) apart[(size_t)t * nparts + g.pf] = sa;
+        }
       }
       // Whole rows back out: instruction i stores rows 2i and 2i + 1.
       u32x4 sv[NI];
@@ -773,7 +927,11 @@ struct EpiSwigluBwd {
 // acc = G = dY W1^T; dU = dRes + r (G * gamma) - r^2 s u; N2 = bf16(r u gamma);
 // gpart[pt, f] = sum over the wave's tokens of r G u (dgamma column partials).
 // ---------------------------------------------------------------------------
-template <bool HAS_RES, bool HAS_N2, bool HAS_GPART>
+// LN: the LayerNorm backward in the same delayed form, with the row
+// statistics a (mean of G * gamma) and s (mean of G * gamma * xhat):
+// dU = dRes + r (G * gamma) - r a - r^2 s (u - mu); N2 = r (u - mu) gamma + beta;
+// gpart sums r G (u - mu) (dgamma) and bgpart sums G (dbeta); beta may be NULL.
+template <bool HAS_RES, bool HAS_N2, bool HAS_GPART, bool LN = false>
 struct EpiRowscaleBwd {
   const uint16_t* u;
   int ldu;
@@ -788,9 +946,21 @@ struct EpiRowscaleBwd {
   int ldn;
   float* gpart;
   int dcols;  // row stride of gpart (= d)
+  const float* mu = nullptr;
+  const float* a = nullptr;
+  const uint16_t* beta = nullptr;
+  float* bgpart = nullptr;
 
   template <int RI, int CI>
   __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+    if constexpr (LN)
+      apply_ln(acc, g);
+    else
+      apply_rms(acc, g);
+  }
+
+  template <int RI, int CI>
+  __device__ __forceinline__ void apply_rms(const f32x16 (&acc)[RI][CI], const Geom& g) const {
     static_assert(CI * 32 == WAVE_T, "column partials assume 128-token wave tiles");
     const Lane L(g);
     const TileView<2> ui(u, ldu, g.tw0, g.fw0);
@@ -881,6 +1051,118 @@ struct EpiRowscaleBwd {
         const int f = L.f(ri, idx >> 3) + (idx & 7);
         const bool ok = L.T > 0 && f < L.F && (g.lt & 1) == 0;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gsum[ri]), gp.rs, gp.off(0, f, ok), 0, 0);
+      }
+    }
+  }
+  // The LayerNorm form: the same walk over 32-feature blocks, with the mean
+  // term and the dbeta column sums.
+  template <int RI, int CI>
+  __device__ __forceinline__ void apply_ln(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+    static_assert(CI * 32 == WAVE_T, "column partials assume 128-token wave tiles");
+    const Lane L(g);
+    const TileView<2> ui(u, ldu, g.tw0, g.fw0);
+    const TileView<2> ri_(dres, ldr, g.tw0, g.fw0);
+    const TileView<2> duo(du, lddu, g.tw0, g.fw0);
+    const TileView<2> n2o(n2, ldn, g.tw0, g.fw0);
+    float rt[CI], c2[CI], mus[CI], ra[CI];
+#pragma unroll
+    for (int ci = 0; ci < CI; ++ci) {
+      const int t = g.tw0 + L.t(ci);
+      rt[ci] = L.tok(ci) ? vload(r, t, g.T) : 0.0f;
+      c2[ci] = rt[ci] * rt[ci] * vload(s, t, g.T);
+      mus[ci] = vload(mu, t, g.T);
+      ra[ci] = rt[ci] * vload(a, t, g.T);
+    }
+    // beta may be NULL: read gamma in its place (always valid) and select 0
+    const bool hb = beta != nullptr;
+    const uint16_t* bsrc = hb ? beta : gamma;
+    float gsum[RI], bsum[RI];
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri) {
+      __builtin_amdgcn_sched_barrier(0);  // one 32-feature block's loads at a time
+      u32x4 gv[2], bev[2], uv[CI][2], rv[CI][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        gv[h] = vload16_bf16(gamma, g.fw0 + L.f(ri, h), g.F);
+        const u32x4 bq = vload16_bf16(bsrc, g.fw0 + L.f(ri, h), g.F);
+        bev[h] = hb ? bq : (u32x4){0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int ci = 0; ci < CI; ++ci)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uv[ci][h] = ui.load16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h));
+          if constexpr (HAS_RES) rv[ci][h] = ri_.load16(L.t(ci), L.f(ri, h), L.ok(ci, ri, h));
+        }
+      float col[16], bcol[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        col[i] = 0.0f;
+        bcol[i] = 0.0f;
+      }
+#pragma unroll
+      for (int ci = 0; ci < CI; ++ci)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bool ok = L.ok(ci, ri, h);
+          float uvv[8], o[8], gm[8], Gv[8];
+          acc8(acc, ri, ci, h, Gv);
+          unpack8(uv[ci][h], uvv);
+          unpack8(gv[h], gm);
+          if constexpr (HAS_RES) {
+            unpack8(rv[ci][h], o);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+          }
+          // rt = 0 outside the matrix, and G = 0 there (zero-filled operands)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float G = Gv[e], cu = uvv[e] - mus[ci];
+            o[e] += rt[ci] * (G * gm[e]) - ra[ci] - c2[ci] * cu;
+            col[h * 8 + e] += rt[ci] * G * cu;
+            bcol[h * 8 + e] += G;
+          }
+          duo.store16(L.t(ci), L.f(ri, h), ok, pack8(o));
+          if constexpr (HAS_N2) {
+            float nv[8], bt[8];
+            unpack8(bev[h], bt);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) nv[e] = fmaf(rt[ci] * (uvv[e] - mus[ci]), gm[e], bt[e]);
+            n2o.store16(L.t(ci), L.f(ri, h), ok, pack8(nv));
+          }
+        }
+      if constexpr (HAS_GPART) {
+        // the transpose-reduce of apply_rms, on both column sums
+#pragma unroll
+        for (int step = 0; step < 4; ++step) {
+          const int mask = 16 >> step;
+          const int n = 16 >> step;
+          const bool upper = (g.lt & mask) != 0;
+#pragma unroll
+          for (int i = 0; i < n / 2; ++i) {
+            const float keep = upper ? col[i + n / 2] : col[i];
+            const float send = upper ? col[i] : col[i + n / 2];
+            col[i] = keep + __shfl_xor(send, mask);
+            const float bkeep = upper ? bcol[i + n / 2] : bcol[i];
+            const float bsend = upper ? bcol[i] : bcol[i + n / 2];
+            bcol[i] = bkeep + __shfl_xor(bsend, mask);
+          }
+        }
+        gsum[ri] = col[0] + __shfl_xor(col[0], 1);
+        bsum[ri] = bcol[0] + __shfl_xor(bcol[0], 1);
+      }
+    }
+    if constexpr (HAS_GPART) {
+      const int idx = g.lt >> 1;
+      const TileView<4> gp(gpart, dcols, g.pt, g.fw0);
+      const TileView<4> bp(bgpart, dcols, g.pt, g.fw0);
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri) {
+        const int f = L.f(ri, idx >> 3) + (idx & 7);
+        const bool ok = L.T > 0 && f < L.F && (g.lt & 1) == 0;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gsum[ri]), gp.rs, gp.off(0, f, ok), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bsum[ri]), bp.rs, bp.off(0, f, ok), 0, 0);
       }
     }
   }

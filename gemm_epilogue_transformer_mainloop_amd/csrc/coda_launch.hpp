@@ -19,8 +19,8 @@ using namespace coda_host;
 // partials, which are laid out per 128-token wave tile).
 template <class Epi>
 struct AnyWaveWidth : std::true_type {};
-template <bool A, bool B, bool C>
-struct AnyWaveWidth<EpiRowscaleBwd<A, B, C>> : std::false_type {};
+template <bool A, bool B, bool C, bool D>
+struct AnyWaveWidth<EpiRowscaleBwd<A, B, C, D>> : std::false_type {};
 
 // Tile-count quantization.  One 256x256 tile per CU at a time: when the tile
 // count leaves the last round of tiles partly empty (8192 x 3072 has 384

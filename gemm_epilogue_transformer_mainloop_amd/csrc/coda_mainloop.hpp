@@ -536,8 +536,12 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
 
 template <int BF, int BT, bool WK, bool XK, class Epi>
 __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi epi) {
-  static_assert(EpiLds<Epi>::value <= lds_bytes<BF, BT, WK, XK>(), "epilogue staging exceeds the LDS");
-  __shared__ __attribute__((aligned(1024))) char smem[lds_bytes<BF, BT, WK, XK>()];
+  // The operand stages, or more when the epilogue stages more (at most the
+  // 160 KiB of a gfx950 CU).
+  constexpr int LDS = EpiLds<Epi>::value > lds_bytes<BF, BT, WK, XK>() ? EpiLds<Epi>::value
+                                                                       : lds_bytes<BF, BT, WK, XK>();
+  static_assert(LDS <= 160 * 1024, "epilogue staging exceeds the LDS");
+  __shared__ __attribute__((aligned(1024))) char smem[LDS];
   gemm_epi_tile<BF, BT, WK, XK, Epi>(p, epi, smem, blockIdx.x, gridDim.x);
 }
 
@@ -547,8 +551,10 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
 template <bool WK, bool XK, class Epi>
 __global__ void __launch_bounds__(NT) gemm_epi_kernel_split(const Problem p, const Problem q, const Epi epi) {
   constexpr int BIG = lds_bytes<256, 256, WK, XK>(), HALF = lds_bytes<256, 128, WK, XK>();
-  static_assert(EpiLds<Epi>::value <= (BIG > HALF ? BIG : HALF), "epilogue staging exceeds the LDS");
-  __shared__ __attribute__((aligned(1024))) char smem[BIG > HALF ? BIG : HALF];
+  constexpr int OPS = BIG > HALF ? BIG : HALF;
+  constexpr int LDS = EpiLds<Epi>::value > OPS ? EpiLds<Epi>::value : OPS;
+  static_assert(LDS <= 160 * 1024, "epilogue staging exceeds the LDS");
+  __shared__ __attribute__((aligned(1024))) char smem[LDS];
   const int nbig = p.nTF * p.nTT;
   if ((int)blockIdx.x < nbig)
     gemm_epi_tile<256, 256, WK, XK, Epi>(p, epi, smem, blockIdx.x, nbig);

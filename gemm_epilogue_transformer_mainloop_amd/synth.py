@@ -184,6 +184,26 @@ def block_inputs(config: int, M: int, d: int, F: int) -> Dict[str, object]:
     }
 
 
+def ln_norm_block_inputs(config: int, M: int, d: int, K: int, N: int, z_mean: float = 0.5) -> Dict[str, object]:
+    """GEMM -> residual -> LayerNorm -> GEMM inputs: those of norm_block_inputs
+    with the residual z ~ N(z_mean, 1) (rows with a nonzero mean exercise the
+    mean term) and a LayerNorm bias beta[d] ~ N(0, 0.1^2)."""
+    out = norm_block_inputs(config, M, d, K, N)
+    out["z"] = normal_bf16(seed_of(config, 2), (M, d), mean=z_mean)
+    out["beta"] = normal_bf16(seed_of(config, 6), (d,), std=0.1)
+    return out
+
+
+def ln_block_inputs(config: int, M: int, d: int, F: int, z_mean: float = 0.5) -> Dict[str, object]:
+    """block_inputs with LayerNorm biases beta_l[d] ~ N(0, 0.1^2) and the
+    residual z ~ N(z_mean, 1)."""
+    out = block_inputs(config, M, d, F)
+    out["z"] = normal_bf16(seed_of(config, 1), (M, d), mean=z_mean)
+    out["beta1"] = normal_bf16(seed_of(config, 10), (d,), std=0.1)
+    out["beta2"] = normal_bf16(seed_of(config, 11), (d,), std=0.1)
+    return out
+
+
 # Full-size shapes of the five workloads (tokens, widths).
 CONFIGS = {
     1: dict(kind="norm_block", M=256, d=512, K=512, N=1024),
