@@ -556,6 +556,17 @@ def bench_all(torch, coda, synth, iters=20):
     rows.append(ent)
     log(json.dumps(ent))
     del wsb
+    for vc in (4096, 8192, 16384):
+        wsv = torch.empty(coda.coda_lmhead_ce_bwd_vchunk_workspace(M, V, d, vc), dtype=torch.uint8, device="cuda")
+        med, mn = time_fn(torch, lambda: coda.coda_lmhead_ce_bwd_vchunk(h, W, labels, lse, 1.0 / M, vc, dH, dW, wsv),
+                          5, 2)
+        ent = {"config": 4, "op": f"lmhead_ce_bwd_vchunk {vc} (3 GEMMs per chunk)", "M": M, "N": V, "K": d,
+               "us_median": med * 1e3, "tflops": 3 * 2.0 * M * V * d / (med * 1e-3) / 1e12,
+               "workspace_bytes": int(wsv.numel())}
+        ent["pct_peak"] = 100 * ent["tflops"] / PEAK_BF16_TFLOPS
+        rows.append(ent)
+        log(json.dumps(ent))
+        del wsv
     L = torch.empty(M, V, dtype=bf, device="cuda")
     rec(4, "lmhead_ce_logits", M, V, d, lambda: coda.coda_lmhead_ce_logits(h, W, labels, lse, lr, lm, L, ws),
         plain_nn(M, V, d))
@@ -708,6 +719,15 @@ def bench_sequences(torch, coda, iters=20):
 
     del wsb
     seq(4, "LM head + CE forward+backward, stored logits", 3 * 2.0 * M * d * V, f_ce_bwd_logits, u_ce_bwd, 3)
+    wsv = torch.empty(coda.coda_lmhead_ce_bwd_vchunk_workspace(M, V, d, 8192), dtype=torch.uint8, device="cuda")
+
+    def f_ce_bwd_vchunk():
+        coda.coda_lmhead_ce(h, W, labels, lse, lr, lm, ws)
+        coda.coda_lmhead_ce_bwd_vchunk(h, W, labels, lse, 1.0 / M, 8192, dH, dW, wsv)
+
+    seq(4, "LM head + CE forward+backward, dlogits in 8192-column vocabulary chunks", 3 * 2.0 * M * d * V,
+        f_ce_bwd_vchunk, u_ce_bwd, 3)
+    del wsv
     del h, W, ws, L, dH, dW
     torch.cuda.empty_cache()
     # config 5: one layer of the block backward (SwiGLU MLP + RMSNorm) at 8B-like shape

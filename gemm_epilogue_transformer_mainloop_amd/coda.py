@@ -55,6 +55,8 @@ _SIGS = {
     "coda_lmhead_ce_bwd": (I, [P, I, P, I, P, P, F, P, I, P, I, P, SZ, I, I, I, P]),
     "coda_lmhead_ce_logits": (I, [P, I, P, I, P, P, P, P, P, I, P, SZ, I, I, I, P]),
     "coda_lmhead_ce_noalloc": (I, [P, I, P, I, P, P, P, P, I, I, I, P]),
+    "coda_lmhead_ce_bwd_vchunk_workspace": (SZ, [I, I, I, I]),
+    "coda_lmhead_ce_bwd_vchunk": (I, [P, I, P, I, P, P, F, P, I, P, I, P, SZ, I, I, I, I, P]),
     "coda_lmhead_ce_noalloc_max_bytes": (SZ, []),
     "coda_lmhead_ce_bwd_logits": (I, [P, I, P, I, P, P, F, P, I, P, I, P, I, I, I, I, P]),
     # LayerNorm variant
@@ -397,6 +399,25 @@ def coda_lmhead_ce_bwd(H, W, labels, lse, grad_scale: float, dH=None, dW=None, w
     _call("coda_lmhead_ce_bwd", _ptr(H), _ld(H), _ptr(W), _ld(W), _ptr(labels), _ptr(lse),
           ctypes.c_float(grad_scale), _ptr(dH), _ld(dH), _ptr(dW), _ld(dW), _ptr(ws), ws.numel() * ws.element_size(),
           M, V, d, _stream())
+    return dH, dW
+
+
+def coda_lmhead_ce_bwd_vchunk_workspace(M: int, V: int, d: int, vchunk: int) -> int:
+    return int(lib().coda_lmhead_ce_bwd_vchunk_workspace(M, V, d, vchunk))
+
+
+def coda_lmhead_ce_bwd_vchunk(H, W, labels, lse, grad_scale: float, vchunk: int = 8192, dH=None, dW=None, ws=None):
+    M, d = H.shape
+    V = W.shape[1]
+    if dH is None:
+        dH = _empty((M, d), torch.bfloat16, H)
+    if dW is None:
+        dW = _empty((d, V), torch.float32, H)
+    if ws is None:
+        ws = _empty((max(coda_lmhead_ce_bwd_vchunk_workspace(M, V, d, vchunk), 256),), torch.uint8, H)
+    _call("coda_lmhead_ce_bwd_vchunk", _ptr(H), _ld(H), _ptr(W), _ld(W), _ptr(labels), _ptr(lse),
+          ctypes.c_float(grad_scale), _ptr(dH), _ld(dH), _ptr(dW), _ld(dW), _ptr(ws), ws.numel() * ws.element_size(),
+          M, V, d, vchunk, _stream())
     return dH, dW
 
 

@@ -119,6 +119,20 @@ __global__ void __launch_bounds__(256) ce_dlogits_kernel(uint16_t* __restrict__ 
   }
 }
 
+// out = bf16(in) for an fp32 [M x N] matrix (N % 8 == 0), 8 elements per
+// thread.
+__global__ void __launch_bounds__(256) f32_to_bf16_kernel(const float* __restrict__ in, int ldi,
+                                                          uint16_t* __restrict__ out, int ldo, int M, int N) {
+  const long long per = N / 8, n = (long long)M * per;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const int row = (int)(i / per), c = (int)(i % per) * 8;
+    const float* p = in + (size_t)row * ldi + c;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+    const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    st16(out + (size_t)row * ldo + c, pack8(v));
+  }
+}
+
 // Deterministic mean of the row losses: one workgroup, fixed-order tree.
 __global__ void __launch_bounds__(1024) mean_kernel(const float* __restrict__ x, int M,
                                                     float* __restrict__ out) {
@@ -263,7 +277,7 @@ coda_status coda_lmhead_ce_bwd(const coda_bf16* H, int ldh, const coda_bf16* W, 
     const int mc = (M - m0) < (int)rows ? (M - m0) : (int)rows;
     const uint16_t* Hc = H + (size_t)m0 * ldh;
     // 1) recompute logits and form dlogits D[mc x V] (bf16) in the epilogue
-    EpiCEBwd e1{labels + m0, lse + m0, grad_scale, D, V};
+    EpiCEBwd<true> e1{labels + m0, lse + m0, grad_scale, D, V};
     if (coda_status s = launch_gemm<false, true>(W, ldw, Hc, ldh, V, mc, d, e1, stream)) return s;
     // 2) dH[mc x d] = D W^T: features = d (rows of W, contiguous along V)
     EpiLinear<false, false> e2{nullptr, nullptr, 0, dH + (size_t)m0 * lddh, lddh};
@@ -271,6 +285,74 @@ coda_status coda_lmhead_ce_bwd(const coda_bf16* H, int ldh, const coda_bf16* W, 
     // 3) dW[d x V] (+)= Hc^T D
     if (coda_status s = coda_gemm_wgrad(Hc, ldh, D, V, dW, lddw, mc, d, V, m0 > 0, stream))
       return s;
+  }
+  return CODA_OK;
+}
+
+// Vocabulary-chunked CE backward: the dlogits chunk [M x vc] bf16 (ld = vc,
+// 256-byte aligned) and, with more than one chunk, the fp32 dH accumulator
+// [M x d] after it.
+static size_t vchunk_d_bytes(int M, int vc) { return ((size_t)M * (size_t)vc * 2 + 255) / 256 * 256; }
+
+size_t coda_lmhead_ce_bwd_vchunk_workspace(int M, int V, int d, int vchunk) {
+  if (M <= 0 || V <= 0 || d <= 0 || vchunk <= 0 || vchunk % 8 != 0) return 0;
+  const int vc = vchunk < V ? vchunk : V;
+  const bool multi = vc < V;
+  return vchunk_d_bytes(M, vc) + (multi ? (size_t)M * (size_t)d * 4 : 0);
+}
+
+coda_status coda_lmhead_ce_bwd_vchunk(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
+                                      const int32_t* labels, const float* lse, float grad_scale, coda_bf16* dH,
+                                      int lddh, float* dW, int lddw, void* ws, size_t ws_bytes, int M, int V, int d,
+                                      int vchunk, hipStream_t stream) {
+  trace("coda_lmhead_ce_bwd_vchunk", "M=%d V=%d d=%d vchunk=%d ws_bytes=%zu", M, V, d, vchunk, ws_bytes);
+  Check c;
+  c.shape(M >= 0 && V >= 0 && d >= 0 && vchunk > 0 && vchunk % 8 == 0);
+  c.bmat(H, ldh, d, M);
+  c.bmat(W, ldw, V, d);
+  c.vec(labels, M, 4);
+  c.vec(lse, M, 4);
+  c.bmat(dH, lddh, d, M);
+  c.fmat(dW, lddw, V, d);
+  c.shape(V % 8 == 0 && d % 8 == 0);
+  if (c.st != CODA_OK) return c.st;
+  if (V == 0 || d == 0) return CODA_OK;
+  if (M > 0 && (ws == nullptr || ((uintptr_t)ws & 255) != 0 ||
+                ws_bytes < coda_lmhead_ce_bwd_vchunk_workspace(M, V, d, vchunk)))
+    return CODA_ERR_WORKSPACE;
+  if (coda_status st = c.device()) return st;
+  if (M == 0)  // no rows: dW = H^T D over an empty reduction = 0
+    return coda_gemm_wgrad(H, ldh, nullptr, V, dW, lddw, 0, d, V, 0, stream);
+  const int vc = vchunk < V ? vchunk : V;
+  const int nch = cdiv(V, vc);
+  uint16_t* D = static_cast<uint16_t*>(ws);
+  float* dh = reinterpret_cast<float*>(static_cast<char*>(ws) + vchunk_d_bytes(M, vc));
+  for (int ch = 0; ch < nch; ++ch) {
+    const int v0 = ch * vc, vcc = (V - v0) < vc ? (V - v0) : vc;
+    // 1) recompute the chunk's logits and form its dlogits D [M x vcc] (bf16,
+    //    ordinary stores: the two GEMMs below read it back from the caches)
+    EpiCEBwd<false> e1{labels, lse, grad_scale, D, vc, v0};
+    if (coda_status s = launch_gemm<false, true>(W + v0, ldw, H, ldh, vcc, M, d, e1, stream)) return s;
+    // 2) dW[:, v0 : v0 + vcc] = H^T D: every column of dW is written once
+    if (coda_status s = coda_gemm_wgrad(H, ldh, D, vc, dW + v0, lddw, M, d, vcc, 0, stream)) return s;
+    // 3) dH (+)= D W[:, chunk]^T: features = d (rows of W, contiguous along V)
+    if (nch == 1) {
+      EpiLinear<false, false> e3{nullptr, nullptr, 0, dH, lddh};
+      if (coda_status s = launch_gemm<true, true>(W + v0, ldw, D, vc, d, M, vcc, e3, stream)) return s;
+    } else if (ch == 0) {
+      EpiF32<false> e3{dh, d};
+      if (coda_status s = launch_gemm<true, true>(W + v0, ldw, D, vc, d, M, vcc, e3, stream)) return s;
+    } else {
+      EpiF32<true> e3{dh, d};
+      if (coda_status s = launch_gemm<true, true>(W + v0, ldw, D, vc, d, M, vcc, e3, stream)) return s;
+    }
+  }
+  if (nch > 1) {
+    const long long n = (long long)M * (d / 8);
+    const long long blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream,
+                       dh, d, dH, lddh, M, d);
+    return launched();
   }
   return CODA_OK;
 }

@@ -716,12 +716,17 @@ struct EpiCE {
 // dlogits of the LM-head cross-entropy backward (recomputed logits):
 // D = (exp(l - lse_t) - [f == label_t]) * scale, bf16.
 // ---------------------------------------------------------------------------
+// NT: non-temporal stores (a dlogits buffer too large to stay in the caches);
+// temporal when the consumer GEMMs read it back from the Infinity Cache.
+// voff: the vocabulary index of the GEMM's feature 0 (vocabulary chunks).
+template <bool NT = true>
 struct EpiCEBwd {
   const int32_t* labels;
   const float* lse;
   float scale;
   uint16_t* D;
   int ldd;
+  int voff = 0;
 
   static constexpr int LDS_BYTES = STAGE_LDS;
 
@@ -740,7 +745,7 @@ struct EpiCEBwd {
     }
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
-      const int label = lab[ci] - g.fw0;
+      const int label = lab[ci] - voff - g.fw0;
       const float Lse = lsev[ci];
 #pragma unroll
       for (int ri = 0; ri < RI; ++ri)
@@ -756,7 +761,7 @@ struct EpiCEBwd {
           stage.put(g, ci, ri, h, pack8(v));
         }
     }
-    stage.flush<CI, true>(g, d);
+    stage.flush<CI, NT>(g, d);
   }
 };
 

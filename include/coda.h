@@ -291,6 +291,29 @@ coda_status coda_lmhead_ce_bwd(const coda_bf16* H, int ldh, const coda_bf16* W, 
                                coda_bf16* dH, int lddh, float* dW, int lddw, void* ws,
                                size_t ws_bytes, int M, int V, int d, hipStream_t stream);
 
+/* The same backward with the dlogits never round-tripping HBM: the
+ * vocabulary is cut into chunks of vchunk columns (vchunk % 8 == 0), and
+ * per chunk
+ *   1) the recompute GEMM's epilogue forms D_c = (exp(l - lse_i) -
+ *      [k == label_i]) grad_scale (bf16, M x vchunk, in ws) with ordinary
+ *      stores, so that the chunk stays in the 256 MB Infinity Cache;
+ *   2) dW[:, chunk] = H^T D_c (fp32; every column of dW is written once);
+ *   3) dH += D_c W[:, chunk]^T, accumulated in fp32 in ws and rounded to bf16
+ *      after the last chunk.
+ * This is the reading notes' cross-entropy (section 2, "Cross-entropy loss")
+ * backward in the form the social thread's third pattern names (the logits
+ * recomputed as in Cut Cross Entropy), with the two consumer GEMMs of each
+ * chunk reading it from the cache instead of HBM.  The default chunk for
+ * M = 8192 is 8192 columns (134 MB of dlogits).  ws: 256-byte aligned,
+ * >= coda_lmhead_ce_bwd_vchunk_workspace(M, V, d, vchunk) bytes. */
+size_t coda_lmhead_ce_bwd_vchunk_workspace(int M, int V, int d, int vchunk);
+
+coda_status coda_lmhead_ce_bwd_vchunk(const coda_bf16* H, int ldh, const coda_bf16* W, int ldw,
+                                      const int32_t* labels, const float* lse, float grad_scale,
+                                      coda_bf16* dH, int lddh, float* dW, int lddw, void* ws,
+                                      size_t ws_bytes, int M, int V, int d, int vchunk,
+                                      hipStream_t stream);
+
 /* The same backward from the logits coda_lmhead_ce_logits kept: an
  * auxiliary kernel overwrites logits (bf16, M x V, ldl) in place with
  *   D = (exp(l - lse_i) - [k == label_i]) grad_scale  (bf16),

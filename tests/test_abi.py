@@ -219,3 +219,21 @@ def test_noalloc_limits(L):
     assert L.coda_lmhead_ce_noalloc(A16, 64, A16b, 128, A16c, A16, None, None, 16, 124, 64, None) == 2
     # no rows: nothing to do
     assert L.coda_lmhead_ce_noalloc(A16, 64, A16b, 128, A16c, A16, None, None, 0, 128, 64, None) == 0
+
+
+def test_vchunk_workspace(L):
+    M, V, d = 8192, 128256, 2048
+    # one chunk of 8192 columns (134 MB) + the fp32 dH accumulator (64 MB)
+    assert coda.coda_lmhead_ce_bwd_vchunk_workspace(M, V, d, 8192) == M * 8192 * 2 + M * d * 4
+    # a chunk as wide as the vocabulary needs no accumulator
+    assert coda.coda_lmhead_ce_bwd_vchunk_workspace(M, V, d, 131072) == M * V * 2
+    assert coda.coda_lmhead_ce_bwd_vchunk_workspace(M, V, d, 100) == 0   # vchunk % 8
+    assert coda.coda_lmhead_ce_bwd_vchunk_workspace(0, V, d, 8192) == 0
+    # workspace too small, then a misaligned one: refused before any device call
+    f = L.coda_lmhead_ce_bwd_vchunk
+    assert f(A16, 64, A16b, 128, A16c, A16, ctypes.c_float(1.0), A16b, 64, A16c, 128, A16, 16, 16, 128, 64, 64,
+             None) == 6
+    assert f(A16, 64, A16b, 128, A16c, A16, ctypes.c_float(1.0), A16b, 64, A16c, 128, ctypes.c_void_p(0x100010),
+             1 << 20, 16, 128, 64, 64, None) == 6
+    assert f(A16, 64, A16b, 128, A16c, A16, ctypes.c_float(1.0), A16b, 64, A16c, 128, A16, 1 << 20, 16, 128, 64, 60,
+             None) == 2

@@ -219,6 +219,21 @@ def test_config4_fullsize_stored_logits(c4_ref):
     check_c4(c4_ref, lse, loss_row, loss_mean, dH, dW, " [stored logits]")
 
 
+def test_config4_fullsize_vchunk(c4_ref):
+    """The vocabulary-chunked backward (8192-column chunks of dlogits, which
+    stay in the Infinity Cache) at the full LM-head shape."""
+    c = S.CONFIGS[4]
+    M, d, V = c["M"], c["d"], c["V"]
+    say(f"case: config 4 full size, vocabulary-chunked backward, M={M} d={d} V={V}")
+    p = c4_ref["p"]
+    coda = C()
+    H, W, lab = dev(p["h"]), dev(p["W"]), dev(p["labels"])
+    lse, loss_row, loss_mean = coda.coda_lmhead_ce(H, W, lab)
+    dH, dW = coda.coda_lmhead_ce_bwd_vchunk(H, W, lab, lse, 1.0 / M, vchunk=8192)
+    torch.cuda.synchronize()
+    check_c4(c4_ref, lse, loss_row, loss_mean, dH, dW, " [vocabulary chunks]")
+
+
 def test_config4_full_vocab_wgrad_small_m():
     """The full 2048 x 128256 weight gradient, exactly, at M = 64 rows."""
     M, d, V = 64, 2048, 128256

@@ -293,6 +293,25 @@ def test_lmhead_ce_fwd_bwd():
     assert_close(dW1.cpu().numpy(), dW_r, "dW (1 chunk)")
 
 
+@pytest.mark.parametrize("vchunk", [256, 1000, 4096])
+def test_lmhead_ce_bwd_vchunk(vchunk):
+    """The vocabulary-chunked backward: 5 chunks with a ragged last one (24
+    columns), 2 chunks (the second 48 columns wide), and a single chunk."""
+    M, d, V = 520, 256, 1048
+    say(f"case: lmhead ce bwd, vocabulary chunks of {vchunk}, M={M} d={d} V={V}")
+    p = S.lmhead_inputs(44, M, d, V)
+    labels = p["labels"].copy()
+    labels[:6] = [0, V - 1, 255, 256, 1023, 1024]
+    coda = C()
+    H, W, lab = dev(p["h"]), dev(p["W"]), dev(labels)
+    lse, _, _ = coda.coda_lmhead_ce(H, W, lab)
+    dH, dW = coda.coda_lmhead_ce_bwd_vchunk(H, W, lab, lse, 1.0 / M, vchunk=vchunk)
+    torch.cuda.synchronize()
+    dh_r, dW_r, _ = O.lmhead_ce_bwd(p["h"].f64(), p["W"].f64(), labels, 1.0 / M)
+    assert_close(f64(dH), dh_r, "dh")
+    assert_close(dW.cpu().numpy(), dW_r, "dW")
+
+
 def test_lmhead_bad_label_is_nan():
     M, d, V = 40, 64, 264
     say("case: lmhead out-of-range label")
