@@ -582,6 +582,9 @@ def bench_all(torch, coda, synth, iters=20):
     M, d, F = 8192, 4096, 14336
     dOut, Wd, Wgu = rnd(M, d), rnd(F, d, std=F ** -0.5), rnd(d, 2 * F, std=d ** -0.5)
     pre, dpre = rnd(M, 2 * F), torch.empty(M, 2 * F, dtype=bf, device="cuda")
+    act5, r5 = torch.empty(M, F, dtype=bf, device="cuda"), torch.ones(M, device="cuda")
+    rec(5, "swiglu+r", M, 2 * F, d, lambda: coda.coda_gemm_swiglu(dOut, Wgu, r5, act5, dpre), plain_nn(M, 2 * F, d))
+    del act5, r5
     spart = torch.empty(M, coda.coda_nparts(F), device="cuda")
     rec(5, "swiglu_bwd+s", M, F, d, lambda: coda.coda_gemm_swiglu_bwd(dOut, Wd, pre, dpre, spart), plain_nt(M, F, d))
     s = torch.empty(M, device="cuda")

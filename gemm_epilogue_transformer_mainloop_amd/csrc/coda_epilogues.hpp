@@ -815,17 +815,18 @@ struct EpiSwigluBwd {
     const Lane L(g);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     char* reg = smem + wave * 32768;
+    const uint32_t lreg = lds_addr(reg);
     const int rlo = g.lane >> 5, pos = g.lane & 31;
     const TileView<2> po(dpre, lddp, g.tw0, 2 * g.fw0);
     const int cols = 2 * L.F;  // pre columns left from the wave tile origin
     auto fetch = [&](int p) {
       const uint16_t* base = pre + (size_t)(g.tw0 + 32 * p) * ldp + 2 * g.fw0;
-      char* buf = reg + (p & 1) * 16384;
+      const uint32_t lbuf = lreg + (uint32_t)((p & 1) * 16384);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int r = 2 * i + rlo, c = pos ^ (r & 7);
         const bool ok = 32 * p + r < L.T && 8 * c < cols;
-        dma16<true>(base, 0x7fffffffu, ok ? (uint32_t)(r * ldp + 8 * c) * 2u : OOB, buf + i * 1024);
+        dma16<true>(base, 0x7fffffffu, ok ? (uint32_t)(r * ldp + 8 * c) * 2u : OOB, lbuf + (uint32_t)(i * 1024));
       }
     };
     [[maybe_unused]] char* cb = smem + 4 * 32768 + wave * 2048;  // LN: c at [0, 1 KiB), b after it

@@ -93,8 +93,15 @@ __device__ __forceinline__ int phi32(int i) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// The 32-bit LDS address of a pointer into the workgroup's LDS.  Converting a
+// generic pointer costs a 64-bit add, a null test and a select; the kernels
+// convert their LDS base once and add offsets to it.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)const_cast<void*>(p);
+}
+
 // One LDS-DMA instruction: 16 bytes per lane from buffer(base, range) at
-// byte offset voff to LDS dst + 16 * lane (dst wave-uniform).  Issued as
+// byte offset voff to LDS address dst + 16 * lane (dst wave-uniform).  Issued as
 // inline assembly so that the compiler's wait insertion does not make every
 // later LDS read wait for all DMA in flight; completion is awaited explicitly
 // (wait_vmcnt) before the barrier that publishes the stage.  vmcnt counts in
@@ -103,7 +110,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // NT marks the load non-temporal (data read once, e.g. an epilogue's input
 // tile), so it does not displace the GEMM operands in the caches.
 template <bool NT = false>
-__device__ __forceinline__ void dma16(const void* base, uint32_t range, uint32_t voff, char* dst) {
+__device__ __forceinline__ void dma16(const void* base, uint32_t range, uint32_t voff, uint32_t dst) {
   typedef __attribute__((ext_vector_type(4))) int i32x4;
   const uint64_t b = reinterpret_cast<uint64_t>(base);
   i32x4 rs;
@@ -111,7 +118,7 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t range, uint32_t
   rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));  // stride 0
   rs[2] = __builtin_amdgcn_readfirstlane((int)range);
   rs[3] = 0x00020000;
-  const int m0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_ptr_t)dst);
+  const int m0 = __builtin_amdgcn_readfirstlane((int)dst);
   // A SALU write of M0 needs one wait state before an LDS-DMA instruction
   // reads it; s_nop 1 gives two.
   if constexpr (NT)
@@ -197,10 +204,11 @@ struct Operand {
   }
 
   // DMA chunk i of the k-tile at k0 into the stage at LDS byte offset `stage`
-  // (wave-uniform: instruction i of wave w writes block 4 i + w).
+  // from the LDS address lds_base (wave-uniform: instruction i of wave w
+  // writes block 4 i + w).
   template <bool MASKED>
   __device__ __forceinline__ void dma(const uint16_t* __restrict__ g, int ld, int row0, int nrows, int k0,
-                                      int K, char* smem_base, int stage, int w, int i) const {
+                                      int K, uint32_t lds_base, int stage, int w, int i) const {
     const uint16_t* base = KMAJ ? g + (size_t)row0 * ld + k0 : g + (size_t)k0 * ld + row0;
     uint32_t off = voff + (uint32_t)i * vstep;
     int range = 0x7fffffff;
@@ -214,8 +222,7 @@ struct Operand {
       const bool in = KMAJ ? (k0 + lcol < K) : (row0 + lcol < nrows);
       off = in ? off : 0x80000000u;
     }
-    char* dst = smem_base + stage + (4 * i + w) * 1024;
-    dma16(base, (uint32_t)range, off, dst);
+    dma16(base, (uint32_t)range, off, lds_base + (uint32_t)(stage + (4 * i + w) * 1024));
   }
 };
 
@@ -344,6 +351,7 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
   OB ob;
   oa.init(p.ldw, wave, lane);
   ob.init(p.ldx, wave, lane);
+  const uint32_t lds0 = lds_addr(smem);
 
   const int nk = (p.K + BK - 1) / BK;
   const bool interior = f0 + BF <= p.F && t0 + BT <= p.T && p.K % BK == 0;
@@ -421,9 +429,9 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
     // DMA instruction d (0..NDMA-1) of the k-tile at k0 into stage `st`.
     auto dma = [&](int k0, int st, int d) {
       if (d < OA::NCH)
-        oa.template dma<MASKED>(p.W, p.ldw, f0, p.F, k0, p.K, smem, st * A_REG, wave, d);
+        oa.template dma<MASKED>(p.W, p.ldw, f0, p.F, k0, p.K, lds0, st * A_REG, wave, d);
       else if (d < NDMA)
-        ob.template dma<MASKED>(p.X, p.ldx, t0, p.T, k0, p.K, smem + B_OFF, st * B_REG, wave, d - OA::NCH);
+        ob.template dma<MASKED>(p.X, p.ldx, t0, p.T, k0, p.K, lds0 + B_OFF, st * B_REG, wave, d - OA::NCH);
     };
 
     // Prologue: k-tiles 0 and 1 into stages 0 and 1.  With no k-tile nothing
