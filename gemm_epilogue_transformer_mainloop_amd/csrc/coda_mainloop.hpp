@@ -180,6 +180,10 @@ struct Operand {
   static_assert(KMAJ || ROWS == 256, "MN-major operands use 256-row tiles");
   static constexpr int REGION = ROWS * BK * 2;           // bytes per stage
   static constexpr int NCH = REGION / (NT * 16);          // DMA instructions per thread
+  // MN-major: instructions [0, NCH/2) fill k-rows 0..31 (k-steps 0 and 1),
+  // which are free for the next k-tile half a k-tile earlier than the rest.
+  // K-major rows hold all 64 k, so the whole region is released at once.
+  static constexpr int NEARLY = KMAJ ? 0 : NCH / 2;
   uint32_t voff = 0;  // byte offset of chunk 0 from the k-tile origin
   uint32_t vstep = 0; // byte offset between chunks i and i+1
   int lrow = 0;       // (masking) row or k-row of chunk 0 relative to the tile origin
@@ -366,11 +370,11 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
   // Fragments are read two k-steps ahead into four register sets (set s
   // holds k-step s), so every fragment of a k-tile is in registers by the
   // start of its step 2: the stage is released there and the DMA of k-tile
-  // kt+2 spreads over steps 2 and 3, DPE instructions per MFMA pair.  The
-  // texture unit takes about 57 B/clk per CU; one k-tile's 64 KiB of DMA
-  // issued within a single k-step (8 pairs) stalls the issuing waves.
+  // kt+2 spreads over steps 2 and 3 (and, for the k-rows of MN-major operands
+  // read by k-steps 0 and 1, over steps 0 and 1).  The texture unit takes
+  // about 57 B/clk per CU; one k-tile's 64 KiB of DMA issued within a single
+  // k-step (8 pairs) stalls the issuing waves.
   bf16x8 fa0[RI], fb0[CI], fa1[RI], fb1[CI], fa2[RI], fb2[CI], fa3[RI], fb3[CI];
-  constexpr int DPE = (NDMA + 2 * NP - 1) / (2 * NP);
 
   // Read n (first-use order: a0, b0.., a1..) of k-step s from `stage` (0/1).
   // MN-major fragments take two transposing reads (n and n+1 of the same
@@ -434,15 +438,48 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
         ob.template dma<MASKED>(p.X, p.ldx, t0, p.T, k0, p.K, lds0 + B_OFF, st * B_REG, wave, d - OA::NCH);
     };
 
-    // Prologue: k-tiles 0 and 1 into stages 0 and 1.  With no k-tile nothing
-    // is loaded (an empty operand may have no storage at all).  Every DMA has
-    // k0 < K and a tile origin inside its matrix.
+    // The DMA of a k-tile in two parts: the early part (the k-rows 0..31 of
+    // MN-major operands) and the late part (the rest).  Part 0 instruction d
+    // (0..NE-1), part 1 instruction d (0..NL-1).
+    constexpr int NE = OA::NEARLY + OB::NEARLY, NL = NDMA - NE;
+    auto dma_part = [&](int k0, int st, int part, int d) {
+      if (part == 0) {
+        if (d < OA::NEARLY) dma(k0, st, d);
+        else dma(k0, st, OA::NCH + d - OA::NEARLY);
+      } else {
+        if (d < OA::NCH - OA::NEARLY) dma(k0, st, OA::NEARLY + d);
+        else dma(k0, st, OA::NCH + OB::NEARLY + d - (OA::NCH - OA::NEARLY));
+      }
+    };
+    // The instructions of one part over the 2 NP MFMA pairs of two k-steps:
+    // those due at pair pw.
+    auto dma_window = [&](int k0, int st, int part, int pw) {
+      constexpr int NPW = 2 * NP;
+      if (part == 0) {
+#pragma unroll
+        for (int d = 0; d < NE; ++d)
+          if ((d * NPW) / NE == pw) dma_part(k0, st, 0, d);
+      } else {
+#pragma unroll
+        for (int d = 0; d < NL; ++d)
+          if ((d * NPW) / NL == pw) dma_part(k0, st, 1, d);
+      }
+    };
+
+    // Prologue: k-tiles 0 and 1 into stages 0 and 1 (each early part, then
+    // late part).  With no k-tile nothing is loaded (an empty operand may have
+    // no storage at all).  Every DMA has k0 < K and a tile origin inside its
+    // matrix.
     if (nk > 0) {
 #pragma unroll
-      for (int d = 0; d < NDMA; ++d) dma(0, 0, d);
+      for (int d = 0; d < NE; ++d) dma_part(0, 0, 0, d);
+#pragma unroll
+      for (int d = 0; d < NL; ++d) dma_part(0, 0, 1, d);
       if (nk > 1) {
 #pragma unroll
-        for (int d = 0; d < NDMA; ++d) dma(BK, 1, d);
+        for (int d = 0; d < NE; ++d) dma_part(BK, 1, 0, d);
+#pragma unroll
+        for (int d = 0; d < NL; ++d) dma_part(BK, 1, 1, d);
         wait_vmcnt<NDMA>();
       } else {
         wait_vmcnt<0>();
@@ -455,19 +492,25 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
     }
 
     // One k-tile: four k-steps of NP MFMA pairs.  Steps 0 and 1 carry the
-    // fragment reads of steps 2 and 3; then wait for k-tile kt+1's DMA and
-    // barrier (every wave holds all of k-tile kt's fragments, so its stage is
-    // free); steps 2 and 3 carry the fragment reads of k-tile kt+1's steps 0
-    // and 1 and the DMA of k-tile kt+2 into the released stage.
-    // sched_barrier fences keep the order.
+    // fragment reads of steps 2 and 3 and the early part of k-tile kt+2's DMA
+    // (its target, k-rows 0..31 of stage kt & 1, was read into registers
+    // during k-tile kt-1; a barrier first makes sure every wave is done).
+    // Then wait for k-tile kt+1's DMA and barrier (every wave holds all of
+    // k-tile kt's fragments, so its stage is free); steps 2 and 3 carry the
+    // fragment reads of k-tile kt+1's steps 0 and 1 and the late part of
+    // k-tile kt+2's DMA.  Per wave the parts are issued in the order E(t),
+    // L(t), E(t+1), L(t+1), ...  sched_barrier fences keep the order.
     auto ktile = [&](int kt, auto has1_c, auto has2_c) {
       constexpr bool HAS1 = decltype(has1_c)::value, HAS2 = decltype(has2_c)::value;
       const int ST = kt & 1, NS = ST ^ 1;
+      const int k2 = (kt + 2) * BK;
+      if constexpr (HAS2 && NE > 0) __syncthreads();
 #pragma unroll
       for (int pr = 0; pr < NP; ++pr) {
         mfma_pair(fa0, fb0, pr);
 #pragma unroll
         for (int r = 0; r < RPP; ++r) read_one(ST, 2, pr * RPP + r, fa2, fb2);
+        if constexpr (HAS2 && NE > 0) dma_window(k2, ST, 0, pr);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -475,11 +518,12 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
         mfma_pair(fa1, fb1, pr);
 #pragma unroll
         for (int r = 0; r < RPP; ++r) read_one(ST, 3, pr * RPP + r, fa3, fb3);
+        if constexpr (HAS2 && NE > 0) dma_window(k2, ST, 0, NP + pr);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (HAS1) wait_vmcnt<0>();
+      // k-tile kt+1 has landed; the early part of kt+2 may still be in flight.
+      if constexpr (HAS1) wait_vmcnt<HAS2 ? NE : 0>();
       __syncthreads();
-      const int k2 = (kt + 2) * BK;
 #pragma unroll
       for (int pr = 0; pr < NP; ++pr) {
         mfma_pair(fa2, fb2, pr);
@@ -487,10 +531,7 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
 #pragma unroll
           for (int r = 0; r < RPP; ++r) read_one(NS, 0, pr * RPP + r, fa0, fb0);
         }
-        if constexpr (HAS2) {
-#pragma unroll
-          for (int r = 0; r < DPE; ++r) dma(k2, ST, pr * DPE + r);
-        }
+        if constexpr (HAS2) dma_window(k2, ST, 1, pr);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -500,10 +541,7 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
 #pragma unroll
           for (int r = 0; r < RPP; ++r) read_one(NS, 1, pr * RPP + r, fa1, fb1);
         }
-        if constexpr (HAS2) {
-#pragma unroll
-          for (int r = 0; r < DPE; ++r) dma(k2, ST, (NP + pr) * DPE + r);
-        }
+        if constexpr (HAS2) dma_window(k2, ST, 1, NP + pr);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
