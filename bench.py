@@ -784,6 +784,87 @@ def bench_block(torch, coda, seq_fn):
 # ----------------------------------------------------------------------------
 
 
+class TimelineRunner:
+    """Runs each op of a step alone with the tile-timeline buffer installed
+    (timeline build of the library) and keeps, per op name, the per-tile
+    figures of every GEMM launch (ops without a GEMM leave no records)."""
+
+    def __init__(self, torch, coda, waves=1 << 16):
+        self.torch, self.coda = torch, coda
+        self.buf = torch.zeros((waves, coda.coda_timeline_words()), dtype=torch.int64, device="cuda")
+        self.rows = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        t.cuda.synchronize()
+        self.buf.zero_()
+        self.coda.coda_timeline_set(self.buf)
+        out = fn()
+        t.cuda.synchronize()
+        self.coda.coda_timeline_set(None)
+        rec = self.buf.cpu().numpy()
+        rec = rec[rec[:, 0] != 0]
+        if len(rec):
+            self.rows.setdefault(name, []).append(timeline_summary(rec))
+        return out
+
+
+def timeline_summary(rec):
+    """Per-launch figures from timeline records (one row per wave; words as in
+    coda_probe.h).  Times in microseconds of the 100 MHz reference clock."""
+    rt, ct = rec[:, 0:4].astype(np.int64), rec[:, 4:8].astype(np.int64)
+    bt, nk, hw, xcc = rec[:, 8], rec[:, 9], rec[:, 10], rec[:, 11]
+    t0 = rt[:, 0].min()
+    us = lambda x: x / 100.0
+    kloop_ct = ct[:, 2] - ct[:, 1]
+    kloop_rt = np.maximum(rt[:, 2] - rt[:, 1], 1)
+    mfma_cyc = 2048.0 * bt / 256.0 * nk  # 4 x 4 (or 4 x 2) MFMA 32x32x16 per k-step, 8 passes of 4 clocks
+    # One record per wave; a tile's four waves run on one compute unit.
+    cu = (xcc.astype(np.int64) << 16) | (((hw >> 13) & 7) << 8) | (((hw >> 12) & 1) << 4) | ((hw >> 8) & 15)
+    wave0 = np.arange(len(rec)) % 4 == 0  # records are dense from block 0: every 4th is a wave 0
+    starts, ends, cus = rt[wave0, 0], rt[wave0, 3], cu[wave0]
+    gaps = []
+    for c in np.unique(cus):
+        i = np.argsort(starts[cus == c])
+        s_, e_ = starts[cus == c][i], ends[cus == c][i]
+        gaps.extend((s_[1:] - e_[:-1]).tolist())
+    span = us(rt[:, 3].max() - t0)
+    ncu = len(np.unique(cus))
+    return {
+        "tiles": int(wave0.sum()), "compute_units": int(ncu), "k_tiles": int(np.median(nk)),
+        "span_us": round(float(span), 1),
+        "prologue_us": round(float(np.median(us(rt[:, 1] - rt[:, 0]))), 2),
+        "kloop_us": round(float(np.median(us(rt[:, 2] - rt[:, 1]))), 2),
+        "epilogue_us": round(float(np.median(us(rt[:, 3] - rt[:, 2]))), 2),
+        "gap_us": round(float(np.median(us(np.array(gaps)))), 2) if gaps else None,
+        "cycles_per_ktile": round(float(np.median(kloop_ct / np.maximum(nk, 1))), 0),
+        "sclk_ghz": round(float(np.median(kloop_ct / kloop_rt * 0.1)), 3),
+        "mfma_issue_in_kloop": round(float(np.median(mfma_cyc / np.maximum(kloop_ct, 1))), 3),
+        "cu_busy": round(float(us(ends - starts).sum() / (ncu * span)), 3),
+    }
+
+
+def timeline_report(torch, coda, synth, out=None):
+    """The headline step's GEMMs, one launch each with the tile timeline."""
+    M, d, F = BLOCK_DIMS
+    p, T = block_inputs_device(torch, synth, M, d, F)
+    fused, _, _ = make_block(torch, coda, T, M, d, F, p["eps"])
+    for _ in range(3):
+        fused()
+    tl = TimelineRunner(torch, coda)
+    fused(tl)
+    lines = []
+    for name, rows in tl.rows.items():
+        for i, r in enumerate(rows):
+            lines.append({"op": name, "launch": i, "shape": BLOCK_SHAPES.get(name), **r})
+    for ln in lines:
+        print(json.dumps(ln), flush=True)
+    if out:
+        with open(out, "w") as f:
+            for ln in lines:
+                f.write(json.dumps(ln) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -794,6 +875,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="headline step only (no unfused sequence, config-2 block, clock probe)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="only print per-tile timelines (prologue, k-loop, epilogue, shader clock) of the headline "
+                         "step's GEMMs, from the timeline build libcoda_timeline.so")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -811,7 +895,13 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.timeline:
+        coda.use_library(coda.TIMELINE_LIB_PATH)
     coda.lib()  # fails loudly if the HIP library is not built
+
+    if args.timeline:
+        timeline_report(torch, coda, synth, args.out)
+        return
 
     if args.copy_calib:
         n = 1 << 30

@@ -1,6 +1,7 @@
 """Build libcoda.so (gfx950) in-tree with hipcc.
 
     python -m gemm_epilogue_transformer_mainloop_amd.build
+    python -m gemm_epilogue_transformer_mainloop_amd.build --timeline   # libcoda_timeline.so
 
 The library is rebuilt on every call: each translation unit is compiled to an
 object in parallel (one hipcc per source), then the objects are linked.
@@ -27,6 +28,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcoda.so")
+TIMELINE_LIB = os.path.join(HERE, "libcoda_timeline.so")
 RESOURCES = os.path.join(HERE, "libcoda.resources.json")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -76,13 +78,19 @@ def _compile(src: str, obj: str, extra: list, verbose: bool) -> str:
     return res.stdout + res.stderr
 
 
-def build(verbose: bool = False, out: str = None, extra: list = None, jobs: int = None) -> str:
-    """Build the library (default: libcoda.so beside this file) and return its path."""
+def build(verbose: bool = False, out: str = None, extra: list = None, jobs: int = None,
+          timeline: bool = False) -> str:
+    """Build the library (default: libcoda.so beside this file) and return its
+    path.  timeline=True builds libcoda_timeline.so instead: the same kernels
+    with the per-wave tile timeline compiled in (CODA_TIMELINE=1)."""
     extra = list(extra or [])
+    if timeline:
+        extra.append("-DCODA_TIMELINE=1")
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    lib = out or LIB
-    os.makedirs(OBJDIR, exist_ok=True)
-    objs = [os.path.join(OBJDIR, os.path.basename(s).replace(".hip", ".o")) for s in srcs]
+    lib = out or (TIMELINE_LIB if timeline else LIB)
+    objdir = OBJDIR + ("_timeline" if timeline else "")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(s).replace(".hip", ".o")) for s in srcs]
     jobs = jobs or min(len(srcs), max(1, len(os.sched_getaffinity(0))))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         texts = list(ex.map(lambda a: _compile(a[0], a[1], extra, verbose), zip(srcs, objs)))
@@ -103,7 +111,7 @@ def build(verbose: bool = False, out: str = None, extra: list = None, jobs: int 
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"link failed ({res.returncode})")
-    if out is None:
+    if out is None and not timeline:
         with open(RESOURCES, "w") as f:
             json.dump(resources, f, indent=1, sort_keys=True)
     os.replace(tmp, lib)
@@ -111,4 +119,4 @@ def build(verbose: bool = False, out: str = None, extra: list = None, jobs: int 
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, timeline="--timeline" in sys.argv[1:]))

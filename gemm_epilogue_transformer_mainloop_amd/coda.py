@@ -18,6 +18,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcoda.so")
+# The same kernels with the tile timeline compiled in (coda_timeline_set).
+TIMELINE_LIB_PATH = os.path.join(_HERE, "libcoda_timeline.so")
 INCLUDE_DIR = os.path.join(os.path.dirname(_HERE), "include")
 HEADER_PATHS = [os.path.join(INCLUDE_DIR, h) for h in ("coda.h", "coda_unfused.h", "coda_probe.h")]
 
@@ -80,6 +82,8 @@ _SIGS = {
     "coda_unfused_cross_entropy_bwd": (I, [P, I, P, P, F, P, I, I, I, P]),
     # include/coda_probe.h
     "coda_probe_mfma": (I, [I, I, P, P]),
+    "coda_timeline_set": (I, [P, I]),
+    "coda_timeline_words": (I, []),
 }
 
 STATUS = {0: "CODA_OK", 1: "CODA_ERR_NULL", 2: "CODA_ERR_SHAPE", 3: "CODA_ERR_ALIGN",
@@ -90,6 +94,14 @@ class CodaError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
         super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status_str(status)})")
+
+
+def use_library(path: str) -> None:
+    """Load `path` (e.g. TIMELINE_LIB_PATH) instead of libcoda.so; only before the first call."""
+    global LIB_PATH
+    if _lib is not None and path != LIB_PATH:
+        raise RuntimeError(f"{LIB_PATH} is already loaded")
+    LIB_PATH = path
 
 
 def lib():
@@ -645,3 +657,19 @@ def coda_probe_mfma(blocks: int, iters: int, out=None):
         out = torch.zeros((blocks, 2), dtype=torch.int64, device="cuda")
     _call("coda_probe_mfma", blocks, iters, _ptr(out), _stream())
     return out
+
+
+def coda_timeline_words() -> int:
+    return lib().coda_timeline_words()
+
+
+def coda_timeline_set(buf=None):
+    """Install the int64 device tensor `buf` [waves, coda_timeline_words()] as
+    the tile-timeline buffer of later GEMM launches (timeline build only);
+    None uninstalls."""
+    if buf is None:
+        _call("coda_timeline_set", None, 0)
+        return
+    assert buf.is_cuda and buf.dtype == torch.int64 and buf.is_contiguous()
+    assert buf.dim() == 2 and buf.shape[1] == coda_timeline_words()
+    _call("coda_timeline_set", _ptr(buf), buf.shape[0])

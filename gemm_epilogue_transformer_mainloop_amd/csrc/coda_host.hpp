@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/coda.h"
 
@@ -143,6 +144,12 @@ struct Check {
     return CODA_OK;
   }
 };
+
+// The timeline buffer of timeline builds (coda_timeline_set), read by every
+// GEMM launch of such a build under g_tl_mu.
+inline std::mutex g_tl_mu;
+inline unsigned long long* g_tl_buf = nullptr;
+inline int g_tl_waves = 0;
 
 // Compute units of the current device, cached per device (0 if unknown).
 inline std::atomic<int> g_cus[64];

@@ -60,6 +60,13 @@ coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, 
   p.nTF = cdiv(F, BF);
   p.nTT = cdiv(T, BT);
   p.f_base = 0;
+  p.tl = nullptr;
+  p.tl_waves = 0;
+  if constexpr (kTimeline) {
+    std::lock_guard<std::mutex> lock(g_tl_mu);
+    p.tl = g_tl_buf;
+    p.tl_waves = g_tl_waves;
+  }
   const int nb = p.nTF * p.nTT;
   if (nb == 0) return CODA_OK;
   if constexpr (BT == 256 && XK && AnyWaveWidth<Epi>::value) {

@@ -50,6 +50,14 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
+// Timeline builds (CODA_TIMELINE=1, a separate library) record per-wave
+// timestamps of every tile; the default build compiles none of it.
+#ifndef CODA_TIMELINE
+#define CODA_TIMELINE 0
+#endif
+constexpr bool kTimeline = CODA_TIMELINE;
+constexpr int TL_WORDS = 12;    // 64-bit words per wave record
+
 constexpr int BK = 64;          // k-tile depth (elements)
 constexpr int NT = 256;         // threads per workgroup (4 waves of 64)
 constexpr int ROW_BYTES = BK * 2;  // one LDS tile row: 64 bf16 = 128 bytes
@@ -259,7 +267,33 @@ struct Problem {
   int F, T, K;        // output features, tokens, reduction length
   int nTF, nTT;       // tile counts along F and T
   int f_base;         // first feature of this launch (tiles cover [f_base, F))
+  unsigned long long* tl;  // timeline records (timeline builds; else null)
+  int tl_waves;            // records tl holds
 };
+
+// Timeline mark `slot` (0 tile start, 1 k-loop start, 2 k-loop end, 3
+// epilogue end) of this wave: record blockIdx.x * 4 + wave holds the
+// reference-clock (100 MHz) stamps in words 0-3, the shader-clock stamps in
+// words 4-7, then the tile's token width, its k-tile count, and the HW_ID and
+// XCC_ID registers (which compute unit ran it).
+__device__ __forceinline__ void timeline_mark(const Problem& p, int slot, int bt, int nk) {
+  if constexpr (kTimeline) {
+    const unsigned long long rt = __builtin_amdgcn_s_memrealtime();
+    const unsigned long long ct = __builtin_amdgcn_s_memtime();
+    const int rec = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if ((threadIdx.x & 63) == 0 && rec < p.tl_waves) {
+      unsigned long long* r = p.tl + (size_t)rec * TL_WORDS;
+      r[slot] = rt;
+      r[4 + slot] = ct;
+      if (slot == 0) {
+        r[8] = (unsigned long long)bt;
+        r[9] = (unsigned long long)nk;
+        r[10] = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID
+        r[11] = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // XCC_ID
+      }
+    }
+  }
+}
 
 // What one lane needs to place its accumulators.
 struct Geom {
@@ -358,6 +392,7 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
   const uint32_t lds0 = lds_addr(smem);
 
   const int nk = (p.K + BK - 1) / BK;
+  timeline_mark(p, 0, BT, nk);
   const bool interior = f0 + BF <= p.F && t0 + BT <= p.T && p.K % BK == 0;
 
   constexpr int NP = RI * CI / 2;           // MFMA pairs per k-step
@@ -548,6 +583,7 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
     using T_ = std::true_type;
     using F_ = std::false_type;
     // k-tile kt lives in LDS stage kt & 1.
+    timeline_mark(p, 1, BT, nk);
     int kt = 0;
     for (; kt + 2 < nk; ++kt) ktile(kt, T_{}, T_{});
     if (kt + 1 < nk) ktile(kt++, T_{}, F_{});
@@ -557,6 +593,7 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
     mainloop(std::false_type{});
   else
     mainloop(std::true_type{});
+  timeline_mark(p, 2, BT, nk);
 
   // The epilogues copy accumulators out of their AGPRs with inline asm, which
   // the compiler's hazard check does not see: 24 wait states cover the
@@ -578,6 +615,7 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
   } else {
     epi.template apply<RI, CI>(acc, g);
   }
+  timeline_mark(p, 3, BT, nk);
 }
 
 template <int BF, int BT, bool WK, bool XK, class Epi>

@@ -68,4 +68,17 @@ coda_status coda_probe_mfma(int blocks, int iters, unsigned long long* out, hipS
   return launched();
 }
 
+coda_status coda_timeline_set(unsigned long long* buf, int waves) {
+  trace("coda_timeline_set", "buf=%p waves=%d", (void*)buf, waves);
+  if (!coda::kTimeline) return CODA_ERR_UNSUPPORTED;
+  if (waves < 0 || (buf == nullptr && waves > 0)) return CODA_ERR_SHAPE;
+  if (buf != nullptr && (reinterpret_cast<uintptr_t>(buf) & 7u) != 0) return CODA_ERR_ALIGN;
+  std::lock_guard<std::mutex> lock(g_tl_mu);
+  g_tl_buf = waves > 0 ? buf : nullptr;
+  g_tl_waves = waves > 0 ? waves : 0;
+  return CODA_OK;
+}
+
+int coda_timeline_words(void) { return coda::TL_WORDS; }
+
 }  // extern "C"

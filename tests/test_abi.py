@@ -237,3 +237,29 @@ def test_vchunk_workspace(L):
              1 << 20, 16, 128, 64, 64, None) == 6
     assert f(A16, 64, A16b, 128, A16c, A16, ctypes.c_float(1.0), A16b, 64, A16c, 128, A16, 1 << 20, 16, 128, 64, 60,
              None) == 2
+
+
+def test_timeline_default_build(L):
+    """The default library compiles no timeline: installing one is refused."""
+    assert L.coda_timeline_words() == 12
+    assert L.coda_timeline_set(None, 0) == 4
+    assert L.coda_timeline_set(A16, 1024) == 4
+
+
+def test_timeline_build_validation():
+    """libcoda_timeline.so: same exports; the buffer is checked before it is installed."""
+    from gemm_epilogue_transformer_mainloop_amd import build
+
+    path = coda.TIMELINE_LIB_PATH
+    if not os.path.exists(path):
+        build.build(timeline=True)
+    T = ctypes.CDLL(path)
+    for name in coda.header_functions():
+        assert hasattr(T, name), name
+    T.coda_timeline_set.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    assert T.coda_timeline_words() == 12
+    assert T.coda_timeline_set(None, 5) == 2                       # NULL with records
+    assert T.coda_timeline_set(A16, -1) == 2
+    assert T.coda_timeline_set(ctypes.c_void_p(0x100004), 8) == 3  # not 8-byte aligned
+    assert T.coda_timeline_set(A16, 8) == 0
+    assert T.coda_timeline_set(None, 0) == 0                       # uninstall
