@@ -16,10 +16,14 @@
  *    losses and weight gradients are fp32.
  *  - All pointers are DEVICE pointers owned by the caller.  The library never
  *    allocates, frees or synchronises; calls are asynchronous and ordered on
- *    `stream` (NULL = default stream).  Its only global state is a per-device
- *    cache of two device properties (the gfx950 check and the compute-unit
- *    count), each written once per device with atomic stores and safe to
- *    read from any thread, and the environment switches below, read once.
+ *    `stream` (NULL = default stream).  Its global state: a per-device cache
+ *    of two device properties (the gfx950 check and the compute-unit count)
+ *    and of the address of the 64 MiB device array behind
+ *    coda_lmhead_ce_noalloc, each written once per device with atomic stores
+ *    and safe to read from any thread; that array itself (one per device,
+ *    held until the process ends); the environment switches below, read
+ *    once; and, in the timeline build only, the timeline buffer installed by
+ *    coda_timeline_set (coda_probe.h), read under a lock.
  *  - Requirements: bf16 base pointers 16-byte aligned and bf16 ld % 8 == 0;
  *    fp32 matrix pointers 16-byte aligned and fp32 ld % 4 == 0; every output
  *    width (N, F, d, V) % 8 == 0, except the SwiGLU activation width F
