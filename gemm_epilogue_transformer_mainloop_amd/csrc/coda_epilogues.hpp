@@ -798,8 +798,10 @@ struct EpiSwigluBwd {
   // linearly and stored as whole row segments.  Phase p+2's DMA goes into
   // phase p's buffer once its rows are back in registers, before its stores,
   // so each phase's data arrives while the previous phase computes and
-  // stores.  Row r keeps its 16-byte chunk c at position c ^ (r & 7), so the
-  // accumulator-layout accesses (32 rows, one chunk) hit distinct banks.
+  // stores.  Row r keeps its 16-byte chunk c at position c ^ (r & 15): the
+  // rows are 512 bytes apart, so every row starts at the same bank, and the
+  // 16 rows that one 16-lane phase of an accumulator-layout access touches
+  // (one chunk each) then cover all 16 bank groups of 16 bytes.
   //
   // Waits: vmcnt retires vector memory operations, loads and stores alike,
   // in issue order (the compiler's own waits on gfx950 rely on it: a load
@@ -824,7 +826,7 @@ struct EpiSwigluBwd {
       const uint32_t lbuf = lreg + (uint32_t)((p & 1) * 16384);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int r = 2 * i + rlo, c = pos ^ (r & 7);
+        const int r = 2 * i + rlo, c = pos ^ (r & 15);
         const bool ok = 32 * p + r < L.T && 8 * c < cols;
         dma16<true>(base, 0x7fffffffu, ok ? (uint32_t)(r * ldp + 8 * c) * 2u : OOB, lbuf + (uint32_t)(i * 1024));
       }
@@ -871,7 +873,7 @@ struct EpiSwigluBwd {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {  // two 16-byte chunks = 4 pairs each
             const int chunk = 8 * ri + 4 * h + 2 * g.hh + c;
-            char* a = buf + r * 512 + ((chunk ^ (r & 7)) << 4);
+            char* a = buf + r * 512 + ((chunk ^ (r & 15)) << 4);
             float pvv[8], out[8];
             unpack8(ld16(a), pvv);
             float cv[8], bv[8];
@@ -921,7 +923,7 @@ struct EpiSwigluBwd {
       }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int rr = 2 * i + rlo, c = pos ^ (rr & 7);
+        const int rr = 2 * i + rlo, c = pos ^ (rr & 15);
         po.store16_nt(32 * p + rr, 8 * c, 32 * p + rr < L.T && 8 * c < cols, sv[i]);
       }
     }
