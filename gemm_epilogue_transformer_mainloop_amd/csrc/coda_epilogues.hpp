@@ -859,14 +859,28 @@ struct EpiSwigluBwd {
                                : 2 * NI + (p + 1 < CI ? NI : 0);
       wait_vmcnt_le(later);
       char* buf = reg + (p & 1) * 16384;
-      // dpre from pre and da in the accumulator layout, in place.
+      // dpre from pre and da in the accumulator layout, in place, in two
+      // halves of the wave tile's features (ri pairs).  Each half's eight
+      // pre chunks are read before any is written back: the writes go to the
+      // same buffer, so the compiler keeps a read after an earlier write, and
+      // reading chunk by chunk left one LDS round trip per chunk exposed
+      // (one wave per SIMD, nothing else to run meanwhile).
       const int ci = p;
       const int r = g.lt;
       float ss = 0.0f, sa = 0.0f;
+      static_assert(RI % 2 == 0, "feature halves of whole 32-row blocks");
 #pragma unroll
-      for (int ri = 0; ri < RI; ++ri)
+      for (int r0 = 0; r0 < RI; r0 += 2) {
+        u32x4 pv[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int j = 0; j < 8; ++j) {
+          const int ri = r0 + (j >> 2), h = (j >> 1) & 1, c = j & 1;
+          const int chunk = 8 * ri + 4 * h + 2 * g.hh + c;
+          pv[j] = ld16(buf + r * 512 + ((chunk ^ (r & 15)) << 4));
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int ri = r0 + (jj >> 1), h = jj & 1;
           const bool ok = L.ok(ci, ri, h);
           float dav[8];
           acc8(acc, ri, ci, h, dav);
@@ -875,7 +889,7 @@ struct EpiSwigluBwd {
             const int chunk = 8 * ri + 4 * h + 2 * g.hh + c;
             char* a = buf + r * 512 + ((chunk ^ (r & 15)) << 4);
             float pvv[8], out[8];
-            unpack8(ld16(a), pvv);
+            unpack8(pv[2 * jj + c], pvv);
             float cv[8], bv[8];
             if constexpr (LN) {
               unpack_f32x8(cb + 32 * chunk, cv);
@@ -886,16 +900,19 @@ struct EpiSwigluBwd {
             for (int q = 0; q < 4; ++q) {
               const float da = dav[4 * c + q];
               const float gg = pvv[2 * q], uu = pvv[2 * q + 1];
+              // With t = g sigma(g) (the SiLU): du = da t and
+              // dg = da u (sigma + t (1 - sigma)), i.e. silu'(g) = sigma (1 + g (1 - sigma)).
               const float sg = sigmoidf_(gg);
-              const float dg = da * uu * sg * (1.0f + gg * (1.0f - sg));
-              const float du = da * gg * sg;
+              const float t = gg * sg;
+              const float du = da * t;
+              const float dg = (da * uu) * (fmaf(-t, sg, t) + sg);
               out[2 * q] = dg;
               out[2 * q + 1] = du;
               if constexpr (LN) {
-                part += dg * (gg - bv[2 * q]) + du * (uu - bv[2 * q + 1]);
-                pa += dg * cv[2 * q] + du * cv[2 * q + 1];
+                part = fmaf(dg, gg - bv[2 * q], fmaf(du, uu - bv[2 * q + 1], part));
+                pa = fmaf(dg, cv[2 * q], fmaf(du, cv[2 * q + 1], pa));
               } else {
-                part += dg * gg + du * uu;
+                part = fmaf(dg, gg, fmaf(du, uu, part));
               }
             }
             ss += ok ? part : 0.0f;
@@ -903,6 +920,7 @@ struct EpiSwigluBwd {
             st16(a, pack8(out));
           }
         }
+      }
       if constexpr (HAS_SPART) {
         ss = sum_halves(ss);
         if constexpr (LN) sa = sum_halves(sa);
