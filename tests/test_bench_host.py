@@ -1,0 +1,85 @@
+"""bench.py's host-side arithmetic, without a GPU: the tile-timeline summary on
+synthetic records with known clocks, the step's FLOP accounting, and the
+traffic entry's source-hash gate."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _records():
+    """Two compute units, two 256x256 tiles each, four waves per tile.
+
+    Per tile: 2 us of prologue, a 10-k-tile k-loop of 16 us that takes 25600
+    shader cycles (1.6 GHz, 2560 cycles per k-tile against 2048 of MFMA
+    work), a 5 us epilogue, and 1 us between a compute unit's tiles."""
+    rows = []
+    for tile_start in (1000, 3400):           # reference ticks (100 MHz)
+        for cu in (0, 1):
+            for _ in range(4):                # waves
+                rt = [tile_start, tile_start + 200, tile_start + 1800, tile_start + 2300]
+                ct = [50000, 50000 + 3200, 50000 + 3200 + 25600, 50000 + 3200 + 25600 + 8000]
+                hw = cu << 8                  # HW_ID: compute unit in bits 11:8
+                rows.append(rt + ct + [256, 10, hw, 3])
+    return np.array(rows, dtype=np.int64)
+
+
+def test_timeline_summary_known_clocks():
+    s = bench.timeline_summary(_records())
+    assert s["tiles"] == 4 and s["compute_units"] == 2 and s["k_tiles"] == 10
+    assert s["prologue_us"] == pytest.approx(2.0)
+    assert s["kloop_us"] == pytest.approx(16.0)
+    assert s["epilogue_us"] == pytest.approx(5.0)
+    assert s["gap_us"] == pytest.approx(1.0)
+    assert s["cycles_per_ktile"] == pytest.approx(2560)
+    assert s["sclk_ghz"] == pytest.approx(1.6)
+    assert s["mfma_issue_in_kloop"] == pytest.approx(0.8)
+    # span 1000 .. 5700 ticks = 47 us; four tiles of 23 us on two compute units
+    assert s["span_us"] == pytest.approx(47.0)
+    assert s["cu_busy"] == pytest.approx(4 * 23.0 / (2 * 47.0), abs=1e-3)
+
+
+def test_timeline_summary_half_tiles():
+    r = _records()
+    r[:, 8] = 128                              # 256 x 128 tiles: half the MFMA work per k-tile
+    s = bench.timeline_summary(r)
+    assert s["mfma_issue_in_kloop"] == pytest.approx(0.4)
+
+
+def test_block_flops():
+    M, d, F = bench.BLOCK_DIMS
+    opf = bench.block_op_flops(M, d, F)
+    assert set(opf) == set(bench.BLOCK_LAUNCHES) == set(bench.BLOCK_SHAPES)
+    total = sum(opf[k] * bench.BLOCK_LAUNCHES[k] for k in opf)
+    # per layer: gate/up 2*M*d*2F and down 2*M*F*d, forward, data and weight gradients (x3);
+    # W0: 2*M*d*d forward, dgrad and wgrad (x3); two layers
+    expect = 2 * 3 * (2 * M * d * 2 * F + 2 * M * F * d) + 3 * 2 * M * d * d
+    assert total == expect
+    assert round(total / 1e12, 2) == 18.14
+    # each op's FLOPs match the M x N x K it reports
+    for k, shape in bench.BLOCK_SHAPES.items():
+        dims = [int(x) for x in shape.split()[0].split("x")]
+        mult = 2 if "twice" in shape else 1
+        assert opf[k] == mult * 2.0 * dims[0] * dims[1] * dims[2], k
+
+
+def test_traffic_entry_needs_current_source(tmp_path, monkeypatch):
+    h = bench.src_hash()
+    assert len(h) == 16 and h == bench.src_hash()   # deterministic over csrc/
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    ent = {"c5 swiglu": {"src_hash": h, "bytes_per_launch": 123}}
+    (prof / "traffic.json").write_text(json.dumps(ent))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))   # profiles/ from tmp_path ...
+    monkeypatch.setattr(bench, "src_hash", lambda: h)   # ... the kernels' hash as before
+    assert bench.load_traffic("c5 swiglu") == 123
+    ent["c5 swiglu"]["src_hash"] = "0" * 16
+    (prof / "traffic.json").write_text(json.dumps(ent))
+    assert bench.load_traffic("c5 swiglu") is None
+    assert bench.load_traffic("missing") is None
