@@ -38,6 +38,7 @@ _SIGS = {
     "coda_nparts": (I, [I]),
     "coda_mparts": (I, [I]),
     "coda_tile_split": (I, [I, I, I]),
+    "coda_tile_split_tokens": (I, [I, I, I]),
     "coda_lmhead_ce_workspace": (SZ, [I, I]),
     "coda_lmhead_ce_bwd_workspace": (SZ, [I, I, I]),
     "coda_gemm": (I, [P, I, P, I, P, I, I, I, I, P]),
@@ -186,6 +187,10 @@ def coda_mparts(M: int) -> int:
 
 def coda_tile_split(F: int, T: int, cus: int) -> int:
     return int(lib().coda_tile_split(F, T, cus))
+
+
+def coda_tile_split_tokens(F: int, T: int, cus: int) -> int:
+    return int(lib().coda_tile_split_tokens(F, T, cus))
 
 
 def coda_lmhead_ce_workspace(M: int, V: int) -> int:

@@ -110,6 +110,13 @@ int coda_tile_split(int F, int T, int cus) {
   if (F <= 0 || T <= 0) return 0;
   return quantization_split(cdiv(F, 256), cdiv(T, 256), cdiv(T, 128), cus);
 }
+int coda_tile_split_tokens(int F, int T, int cus) {
+  if (F <= 0 || T <= 0 || cus <= 0) return 0;
+  const int nTF = cdiv(F, 256), nTT = cdiv(T, 256);
+  if (coda_tile_split(F, T, cus) > 0) return 0;                    // the feature split applies
+  if (2 * nTF * nTT <= cus && cdiv(T, 128) > nTT) return 0;        // all 256 x 128 tiles
+  return token_split(nTF, nTT, T, cus);
+}
 
 
 coda_status coda_row_rms(const float* part, int nparts, int M, int d, float eps, float* r,

@@ -45,6 +45,29 @@ inline int quantization_split(int nTF, int nTT, int nTT_half, int cus) {
   return split;
 }
 
+// Token split: when the feature split finds nothing, the trailing token
+// range can be covered by 256 x 128 tiles instead (the weight gradient
+// 14336 x 4096 over 8192 tokens has 56 x 16 = 896 tiles, 3.5 rounds: 48 token
+// tiles x 16 = 768 big tiles are 3 rounds, the last 2048 tokens 256 half
+// tiles, one round of 0.6).  Returns the number of 256-token tiles to keep
+// big, or 0.  Same cost model as the feature split; of equal costs the one
+// with the most big tiles.
+inline int token_split(int nTF, int nTT, int T, int cus) {
+  if (cus <= 0 || nTT < 2) return 0;
+  const double base = (double)cdiv(nTF * nTT, cus);
+  double best = base - 0.2;
+  int split = 0;
+  for (int tb = nTT - 1; tb >= 1; --tb) {
+    const int nh = cdiv(T - 256 * tb, 128);
+    const double c = (double)cdiv(nTF * tb, cus) + 0.6 * (double)cdiv(nTF * nh, cus);
+    if (c < best) {
+      best = c;
+      split = tb;
+    }
+  }
+  return split;
+}
+
 template <bool WK, bool XK, int BT = 256, class Epi>
 coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, int F, int T, int K,
                         const Epi& epi, hipStream_t stream) {
@@ -60,6 +83,7 @@ coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, 
   p.nTF = cdiv(F, BF);
   p.nTT = cdiv(T, BT);
   p.f_base = 0;
+  p.t_base = 0;
   p.tl = nullptr;
   p.tl_waves = 0;
   if constexpr (kTimeline) {
@@ -69,7 +93,7 @@ coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, 
   }
   const int nb = p.nTF * p.nTT;
   if (nb == 0) return CODA_OK;
-  if constexpr (BT == 256 && XK && AnyWaveWidth<Epi>::value) {
+  if constexpr (BT == 256 && AnyWaveWidth<Epi>::value) {
     const int cus = device_cus();
     const int split = coda_tile_split(F, T, cus);
     if (split > 0) {
@@ -91,6 +115,16 @@ coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, 
       half.nTT = cdiv(T, 128);
       hipLaunchKernelGGL((gemm_epi_kernel_split<WK, XK, Epi>), dim3(half.nTF * half.nTT), dim3(NT), 0,
                          stream, none, half, epi);
+      return launched();
+    }
+    const int tsplit = coda_tile_split_tokens(F, T, cus);
+    if (tsplit > 0) {
+      Problem big = p, half = p;
+      big.nTT = tsplit;
+      half.t_base = tsplit * 256;
+      half.nTT = cdiv(T - half.t_base, 128);
+      hipLaunchKernelGGL((gemm_epi_kernel_split<WK, XK, Epi>), dim3(big.nTF * big.nTT + half.nTF * half.nTT),
+                         dim3(NT), 0, stream, big, half, epi);
       return launched();
     }
   }

@@ -29,7 +29,7 @@
 // XOR-swizzled by (k & 3) << 1) and its fragments come from two transposing
 // reads (ds_read_b64_tr_b16): within a group of 16 lanes, lane j receives
 // element j % 4 of the 8 bytes addressed by lane j / 4 + 4 m (m = 0..3).  All
-// DMA writes cover whole 128/512-byte global rows per instruction, and every
+// DMA writes cover whole 128/256/512-byte global rows per instruction, and every
 // fragment read phase touches each LDS bank once.  Out-of-matrix chunks use an
 // offset beyond the descriptor's range, for which the hardware writes zeros.
 //
@@ -177,15 +177,15 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
 // K-major (element (row, k) at g[row * ld + k]): block 4i+w holds rows
 //   (4i+w)*8 .. +7; lane l loads row (4i+w)*8 + l/8, logical chunk
 //   (l%8) ^ sw(row), sw(row) = (row >> 1) & 7 = (4w + l/16) & 7.
-// MN-major (element (row, k) at g[k * ld + row], ROWS = 256): block 4i+w holds
-//   k-rows (4i+w)*2 .. +1 (512 bytes each); lane l loads k-row (4i+w)*2 + l/32,
-//   logical chunk c with 32-byte block (p/2) ^ ((k & 3) << 1), p = l % 32.
+// MN-major (element (row, k) at g[k * ld + row]): k-rows of 2 ROWS bytes, KPR =
+//   1024 / (2 ROWS) of them per block: block 4i+w holds k-rows (4i+w)*KPR ..
+//   +KPR-1; lane l loads k-row (4i+w)*KPR + l/(64/KPR), logical chunk c with
+//   32-byte block (p/2) ^ ((k & 3) << 1), p = l % (64/KPR).
 // ---------------------------------------------------------------------------
 
 template <int ROWS, bool KMAJ>
 struct Operand {
   static_assert(ROWS == 128 || ROWS == 256, "tile rows");
-  static_assert(KMAJ || ROWS == 256, "MN-major operands use 256-row tiles");
   static constexpr int REGION = ROWS * BK * 2;           // bytes per stage
   static constexpr int NCH = REGION / (NT * 16);          // DMA instructions per thread
   // MN-major: instructions [0, NCH/2) fill k-rows 0..31 (k-steps 0 and 1),
@@ -206,12 +206,14 @@ struct Operand {
       voff = (uint32_t)(row * ld + c * 8) * 2u;
       vstep = (uint32_t)(32 * ld) * 2u;
     } else {
-      const int kr = w * 2 + (l >> 5), pp = l & 31;
+      // KPR k-rows of 2 ROWS bytes per 1 KiB block, 64 / KPR lanes per k-row.
+      constexpr int KPR = 1024 / (2 * ROWS), LPK = 64 / KPR;
+      const int kr = w * KPR + l / LPK, pp = l % LPK;
       const int c = (((pp >> 1) ^ ((kr & 3) << 1)) << 1) | (pp & 1);
       lrow = kr;
       lcol = c * 8;
       voff = (uint32_t)(kr * ld + c * 8) * 2u;
-      vstep = (uint32_t)(8 * ld) * 2u;
+      vstep = (uint32_t)(4 * KPR * ld) * 2u;
     }
   }
 
@@ -246,14 +248,14 @@ struct Operand {
 __device__ __forceinline__ int kmaj_frag_off(int row, int hh) {
   return row * 128 + ((hh ^ ((row >> 1) & 7)) << 4);
 }
-template <bool PHI>
+template <bool PHI, int PITCH = 512>
 __device__ __forceinline__ int mnmaj_frag_off(int row0, int lane) {
   const int G = lane >> 4, q = lane & 15;
   const int kr = 8 * (G >> 1) + (q >> 2);
   const int r = 16 * (G & 1) + 4 * (q & 3);
   const int f = row0 + (PHI ? phi32(r) : r);
   const int blk = f >> 4;
-  return kr * 512 + ((blk ^ ((kr & 3) << 1)) << 5) + ((f & 15) << 1);
+  return kr * PITCH + ((blk ^ ((kr & 3) << 1)) << 5) + ((f & 15) << 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -267,6 +269,7 @@ struct Problem {
   int F, T, K;        // output features, tokens, reduction length
   int nTF, nTT;       // tile counts along F and T
   int f_base;         // first feature of this launch (tiles cover [f_base, F))
+  int t_base;         // first token of this launch (tiles cover [t_base, T))
   unsigned long long* tl;  // timeline records (timeline builds; else null)
   int tl_waves;            // records tl holds
 };
@@ -361,6 +364,7 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
   using OB = Operand<BT, XK>;
   // LDS: A stage 0 | A stage 1 | B stage 0 | B stage 1
   constexpr int A_REG = OA::REGION, B_REG = OB::REGION, B_OFF = 2 * A_REG;
+  constexpr int A_PITCH = 2 * BF, B_PITCH = 2 * BT;  // MN-major k-row bytes
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -368,7 +372,7 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
   const int lt = lane & 31, hh = lane >> 5;
   int tf, tt;
   tile_coords(bid, nb, p.nTF, p.nTT, tf, tt);
-  const int f0 = p.f_base + tf * BF, t0 = tt * BT;
+  const int f0 = p.f_base + tf * BF, t0 = p.t_base + tt * BT;
 
   f32x16 acc[RI][CI];
 #pragma unroll
@@ -380,10 +384,10 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
   int a_off[RI], b_off[CI];
 #pragma unroll
   for (int i = 0; i < RI; ++i)
-    a_off[i] = WK ? kmaj_frag_off(wf * WF + i * 32 + phi32(lt), hh) : mnmaj_frag_off<true>(wf * WF + i * 32, lane);
+    a_off[i] = WK ? kmaj_frag_off(wf * WF + i * 32 + phi32(lt), hh) : mnmaj_frag_off<true, A_PITCH>(wf * WF + i * 32, lane);
 #pragma unroll
   for (int j = 0; j < CI; ++j)
-    b_off[j] = B_OFF + (XK ? kmaj_frag_off(wt * WT + j * 32 + lt, hh) : mnmaj_frag_off<false>(wt * WT + j * 32, lane));
+    b_off[j] = B_OFF + (XK ? kmaj_frag_off(wt * WT + j * 32 + lt, hh) : mnmaj_frag_off<false, B_PITCH>(wt * WT + j * 32, lane));
 
   OA oa;
   OB ob;
@@ -438,7 +442,7 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
       } else {
         typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
         const bf16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4*)(lds_ptr_t)(smem + a_off[q] + stage * A_REG + (16 * s + 4 * u) * 512));
+            (__attribute__((address_space(3))) bf16x4*)(lds_ptr_t)(smem + a_off[q] + stage * A_REG + (16 * s + 4 * u) * A_PITCH));
 #pragma unroll
         for (int e = 0; e < 4; ++e) a[q][4 * u + e] = h[e];
       }
@@ -449,7 +453,7 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
       } else {
         typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
         const bf16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4*)(lds_ptr_t)(smem + b_off[j] + stage * B_REG + (16 * s + 4 * u) * 512));
+            (__attribute__((address_space(3))) bf16x4*)(lds_ptr_t)(smem + b_off[j] + stage * B_REG + (16 * s + 4 * u) * B_PITCH));
 #pragma unroll
         for (int e = 0; e < 4; ++e) b[j][4 * u + e] = h[e];
       }

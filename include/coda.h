@@ -98,13 +98,21 @@ int coda_mparts(int M);
  * 256 * split on are computed in 256 x 128 tiles by the same dispatch.
  * Returns split (0: no such split).  A problem of at most cus/2 tiles of
  * 256 x 256 (under half a round) instead runs entirely in 256 x 128 tiles,
- * on twice as many compute units.  Both apply to coda_gemm, the forward
- * calls, coda_gemm_swiglu_bwd, coda_gemm_res_sumsq_bwd (dX) and the GEMMs
- * of the LM head; coda_gemm_rowscale_bwd and the weight gradients always use
- * 256 x 256 tiles.  This plans the fixed mainloop that every call shares
+ * on twice as many compute units.  Both apply to every GEMM of the library
+ * except coda_gemm_rowscale_bwd, whose dgamma column partials are laid out
+ * per 256-token tile.  This plans the fixed mainloop that every call shares
  * (paper abstract and Figure 3: the mainloop stays as it is and only the
  * epilogue changes).  Host-only: touches no device. */
 int coda_tile_split(int F, int T, int cus);
+
+/* When neither of the above applies: the number tb of 256-token tiles that
+ * stay 256 x 256, the tokens from 256 * tb on being computed in 256 x 128
+ * tiles by the same dispatch (0: no such split).  It is chosen with the same
+ * round-count model (a 256 x 128 tile costs 0.6 of a 256 x 256 one) and must
+ * save 0.2 rounds, as for the weight gradient 14336 x 4096 over 8192 tokens
+ * (3.5 rounds of 256 x 256 tiles: tb = 48 gives 3 + 0.6).  Same scope as
+ * coda_tile_split.  Host-only: touches no device. */
+int coda_tile_split_tokens(int F, int T, int cus);
 
 /* Workspace bytes coda_lmhead_ce needs for M rows and vocabulary V: the
  * per-tile max and sum-exp statistics and the gathered target logits that

@@ -263,3 +263,23 @@ def test_timeline_build_validation():
     assert T.coda_timeline_set(ctypes.c_void_p(0x100004), 8) == 3  # not 8-byte aligned
     assert T.coda_timeline_set(A16, 8) == 0
     assert T.coda_timeline_set(None, 0) == 0                       # uninstall
+
+
+def test_tile_split_tokens(L):
+    """The token split: only when neither the feature split nor the all-half-
+    tile plan applies, the largest token-tile count that saves 0.2 rounds."""
+    f = coda.coda_tile_split_tokens
+    assert f(4096, 14336, 256) == 48      # weight gradient dWd: 3.5 rounds -> 3 + 0.6
+    assert f(4096, 14000, 256) == 48      # ragged: 47 and 48 cost the same; the larger
+    assert f(28672, 8192, 256) == 0       # 14 whole rounds
+    assert f(3072, 8192, 256) == 0 and coda.coda_tile_split(3072, 8192, 256) == 8   # the feature split
+    assert f(512, 1000, 256) == 0         # 8 tiles: all 256 x 128
+    assert f(4096, 14336, 0) == 0 and f(0, 14336, 256) == 0 and f(4096, 0, 256) == 0
+    # the cost model, restated: big rounds + 0.6 x half-tile rounds, 0.2 rounds saved
+    cdiv = lambda a, b: -(-a // b)
+    for F, T in [(4096, 14336), (4096, 14000), (1000, 9000), (2304, 30000)]:
+        t = f(F, T, 256)
+        if t:
+            nTF, nTT = cdiv(F, 256), cdiv(T, 256)
+            cost = cdiv(nTF * t, 256) + 0.6 * cdiv(nTF * cdiv(T - 256 * t, 128), 256)
+            assert cost <= cdiv(nTF * nTT, 256) - 0.2

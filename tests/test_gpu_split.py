@@ -136,3 +136,61 @@ def test_split_lmhead_ce():
     dh_r, dW_r, _ = O.lmhead_ce_bwd(h.f64(), W.f64(), labels, 1.0 / M)
     assert_close(f64(dH), dh_r, "dh")
     assert_close(dW.cpu().numpy(), dW_r, "dW")
+
+
+def plan(F, T):
+    """The tile plan on this device: ("feature", split), ("small", 0), ("token", split) or ("none", 0)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    s = C().coda_tile_split(F, T, cus)
+    if s > 0:
+        return "feature", s
+    nTF, nTT = -(-F // 256), -(-T // 256)
+    if 2 * nTF * nTT <= cus and -(-T // 128) > nTT:
+        return "small", 0
+    t = C().coda_tile_split_tokens(F, T, cus)
+    return ("token", t) if t > 0 else ("none", 0)
+
+
+def test_token_split_gemm():
+    """Forward GEMM whose plan is the token split: 4096 features (16 tiles) x
+    14000 tokens (55 tiles, 3.4 rounds): tokens 0..12287 in 256 x 256 tiles,
+    the rest (1712, the last half tile ragged) in 256 x 128 tiles."""
+    Mt, Kt, Nt = 14000, 136, 4096
+    kind, s = plan(Nt, Mt)
+    say(f"case: token split gemm M={Mt} N={Nt} K={Kt}: plan {kind} {s}")
+    assert kind == "token" and s == 48
+    A = S.normal_bf16(731, (Mt, Kt))
+    W = S.normal_bf16(732, (Kt, Nt), std=Kt ** -0.5)
+    Y = C().coda_gemm(dev(A), dev(W))
+    torch.cuda.synchronize()
+    assert_close(f64(Y), O.gemm(A.f64(), W.f64()), "Y")
+
+
+# (N output columns = features, K_in rows of dW = tokens of the launch, plan)
+WGRAD_PLANS = [(712, 24504, "feature"), (4096, 14000, "token"), (512, 1000, "small")]
+
+
+@pytest.mark.parametrize("N,Kin,kind", WGRAD_PLANS)
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_split_wgrad(N, Kin, kind, accumulate):
+    """The weight gradient dW = X^T dY (both operands contiguous along the
+    output dims) under each tile plan, now that its token operand also has a
+    128-row tile: the 256 x 128 tiles read it through 256-byte k-rows.  The
+    reduction (200 tokens) is not a multiple of 64."""
+    Mr = 200
+    got, s = plan(N, Kin)
+    say(f"case: wgrad N={N} Kin={Kin} M={Mr} accumulate={accumulate}: plan {got} {s}")
+    assert got == kind
+    X = S.normal_bf16(741, (Mr, Kin))
+    dY = S.normal_bf16(742, (Mr, N))
+    ref = O.gemm(X.f64().T, dY.f64())
+    coda = C()
+    if accumulate:
+        base = np.random.default_rng(743).standard_normal((Kin, N)).astype(np.float32)
+        dW = torch.from_numpy(base).cuda()
+        coda.coda_gemm_wgrad(dev(X), dev(dY), dW, accumulate=True)
+        ref = ref + base.astype(np.float64)
+    else:
+        dW = coda.coda_gemm_wgrad(dev(X), dev(dY))
+    torch.cuda.synchronize()
+    assert_close(dW.double().cpu().numpy(), ref, "dW")
