@@ -1,10 +1,13 @@
-"""GPU parity of the tile-count split: when 256x256 tiles leave the last round
-mostly empty, the trailing features run as 256x128 tiles in a second launch
-(coda_tile_split).  Every call that can split is run at a shape that splits on
-the device (asserted), with ragged tokens (M = 24500: the last 128-token tile
-holds 52 rows), ragged features (712 = 2 x 256 + 200, so the half tiles start
-at feature 512 and end mid-tile) and a K that is not a multiple of 64, against
-the fp64 oracle.  Bound: max|gpu - ref| <= 2e-2 * max|ref|.
+"""GPU parity of the tile plans: when 256x256 tiles leave the last round
+mostly empty, the trailing features (coda_tile_split) or the trailing tokens
+(coda_tile_split_tokens) run as 256x128 tiles in the same dispatch, and a
+problem of under half a round runs in 256x128 tiles only.  Every call that can
+split is run at a shape that splits on the device (asserted), with ragged
+tokens (M = 24500: the last 128-token tile holds 52 rows), ragged features
+(712 = 2 x 256 + 200, so the half tiles start at feature 512 and end mid-tile)
+and a K that is not a multiple of 64; the weight gradient runs under each plan,
+plain and accumulating.  Against the fp64 oracle; bound: max|gpu - ref| <=
+2e-2 * max|ref|.
 """
 
 import numpy as np
