@@ -872,6 +872,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--all", action="store_true", help="also time every fused call of the five workloads")
     ap.add_argument("--out", default=None, help="file for the --all table (JSON lines)")
+    ap.add_argument("--iters", type=int, default=20,
+                    help="timed calls per --all entry (after 3-5 untimed ones); fewer for counter runs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="headline step only (no unfused sequence, config-2 block, clock probe)")
@@ -1044,7 +1046,7 @@ def main():
 
     if args.all:
         torch.cuda.empty_cache()
-        rows = bench_all(torch, coda, synth)
+        rows = bench_all(torch, coda, synth, max(1, args.iters))
         if args.out:
             with open(args.out, "w") as f:
                 for r_ in rows:
