@@ -154,14 +154,20 @@ def plan(F, T):
     return ("token", t) if t > 0 else ("none", 0)
 
 
-def test_token_split_gemm():
-    """Forward GEMM whose plan is the token split: 4096 features (16 tiles) x
-    14000 tokens (55 tiles, 3.4 rounds): tokens 0..12287 in 256 x 256 tiles,
-    the rest (1712, the last half tile ragged) in 256 x 128 tiles."""
-    Mt, Kt, Nt = 14000, 136, 4096
+# (tokens M, K, features N, big token tiles): 14000 tokens = 55 tiles, 3.4 rounds of
+# 16 feature tiles: tokens 0..12287 in 256 x 256 tiles, the rest (1712, the last
+# half tile ragged) in 256 x 128 tiles; the others split 20000 (79 token tiles),
+# 6000 (24, a 1.5-round problem) and 20000 again at 24 feature tiles; K from 1 to
+# 9 k-tiles of 64, never a multiple of 64 but at 8.
+TOKEN_SPLITS = [(14000, 136, 4096, 48), (20000, 72, 2048, 64), (6000, 520, 4096, 16), (20000, 8, 6144, 74)]
+
+
+@pytest.mark.parametrize("Mt,Kt,Nt,tb", TOKEN_SPLITS)
+def test_token_split_gemm(Mt, Kt, Nt, tb):
+    """Forward GEMM whose plan is the token split."""
     kind, s = plan(Nt, Mt)
     say(f"case: token split gemm M={Mt} N={Nt} K={Kt}: plan {kind} {s}")
-    assert kind == "token" and s == 48
+    assert kind == "token" and s == tb
     A = S.normal_bf16(731, (Mt, Kt))
     W = S.normal_bf16(732, (Kt, Nt), std=Kt ** -0.5)
     Y = C().coda_gemm(dev(A), dev(W))
@@ -170,7 +176,7 @@ def test_token_split_gemm():
 
 
 # (N output columns = features, K_in rows of dW = tokens of the launch, plan)
-WGRAD_PLANS = [(712, 24504, "feature"), (4096, 14000, "token"), (512, 1000, "small")]
+WGRAD_PLANS = [(712, 24504, "feature"), (4096, 14000, "token"), (4096, 6000, "token"), (512, 1000, "small")]
 
 
 @pytest.mark.parametrize("N,Kin,kind", WGRAD_PLANS)
@@ -197,3 +203,32 @@ def test_split_wgrad(N, Kin, kind, accumulate):
         dW = coda.coda_gemm_wgrad(dev(X), dev(dY))
     torch.cuda.synchronize()
     assert_close(dW.double().cpu().numpy(), ref, "dW")
+
+
+def test_token_split_fused():
+    """Fused epilogues under the token split (the half tiles start at token
+    12288): SwiGLU forward (act and pre, 4096 interleaved gate/up features)
+    and res_sumsq (u, h2 and the per-128-feature row partials), at 14000
+    ragged tokens and K = 136."""
+    Mt, Kt = 14000, 136
+    coda = C()
+    kind, s = plan(4096, Mt)
+    say(f"case: token split swiglu + res_sumsq M={Mt} N=4096 K={Kt}: plan {kind} {s}")
+    assert kind == "token"
+    A = S.normal_bf16(751, (Mt, Kt))
+    Wgu = S.normal_bf16(752, (Kt, 4096), std=Kt ** -0.5)
+    act, pre = coda.coda_gemm_swiglu(dev(A), dev(Wgu))
+    torch.cuda.synchronize()
+    t = O.gemm(A.f64(), Wgu.f64())
+    assert_close(f64(pre), t, "pre")
+    assert_close(f64(act), O.swiglu(t), "act")
+    del act, pre, t
+    W0 = S.normal_bf16(753, (Kt, 4096), std=Kt ** -0.5)
+    z = S.normal_bf16(754, (Mt, 4096))
+    g = S.normal_bf16(755, (4096,), std=0.1, mean=1.0)
+    U, H2, part = coda.coda_gemm_res_sumsq(dev(A), dev(W0), dev(z), dev(g))
+    torch.cuda.synchronize()
+    u, h2, ss = O.res_sumsq(A.f64(), W0.f64(), z.f64(), g.f64())
+    assert_close(f64(U), u, "u")
+    assert_close(f64(H2), h2, "h2")
+    assert_close(part.double().sum(1).cpu().numpy(), ss, "sum of partials")
