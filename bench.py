@@ -532,6 +532,8 @@ def bench_all(torch, coda, synth, iters=20):
     dpre = torch.empty(M, 2 * F, dtype=bf, device="cuda")
     rec(3, "swiglu_bwd", M, F, d, lambda: coda.coda_gemm_swiglu_bwd(dY, Wd, pre, dpre, want_spart=False),
         plain_nt(M, F, d))
+    rec(3, "swiglu_bwd overlap", M, F, d,
+        lambda: coda.coda_gemm_swiglu_bwd_overlap(dY, Wd, pre, dpre, want_spart=False), plain_nt(M, F, d))
     dX = torch.empty(M, d, dtype=bf, device="cuda")
     rec(3, "dgrad+residual", M, d, 2 * F, lambda: coda.coda_gemm_res_sumsq_bwd(dpre, Wgu, dRes=dY, dX=dX, want_dw=False),
         plain_nt(M, d, 2 * F))
@@ -587,6 +589,8 @@ def bench_all(torch, coda, synth, iters=20):
     del act5, r5
     spart = torch.empty(M, coda.coda_nparts(F), device="cuda")
     rec(5, "swiglu_bwd+s", M, F, d, lambda: coda.coda_gemm_swiglu_bwd(dOut, Wd, pre, dpre, spart), plain_nt(M, F, d))
+    rec(5, "swiglu_bwd+s overlap", M, F, d, lambda: coda.coda_gemm_swiglu_bwd_overlap(dOut, Wd, pre, dpre, spart),
+        plain_nt(M, F, d))
     s = torch.empty(M, device="cuda")
     rec(5, "row_rms_bwd", M, 0, 0, lambda: coda.coda_row_rms_bwd(spart, d, s), aux_bytes=spart.numel() * 4 + M * 4)
     u, gam, r = rnd(M, d), torch.ones(d, dtype=bf, device="cuda"), torch.ones(M, device="cuda")
@@ -830,11 +834,17 @@ def timeline_summary(rec):
         gaps.extend((s_[1:] - e_[:-1]).tolist())
     span = us(rt[:, 3].max() - t0)
     ncu = len(np.unique(cus))
+    # the first round of tiles (records of the first ncu tiles) against the rest
+    first = np.arange(len(rec)) < 4 * ncu
+    kl = us(rt[:, 2] - rt[:, 1])
+    rest = float(np.median(kl[~first])) if (~first).any() else None
     return {
         "tiles": int(wave0.sum()), "compute_units": int(ncu), "k_tiles": int(np.median(nk)),
         "span_us": round(float(span), 1),
         "prologue_us": round(float(np.median(us(rt[:, 1] - rt[:, 0]))), 2),
         "kloop_us": round(float(np.median(us(rt[:, 2] - rt[:, 1]))), 2),
+        "kloop_us_first_round": round(float(np.median(kl[first])), 2),
+        "kloop_us_later_rounds": round(rest, 2) if rest is not None else None,
         "epilogue_us": round(float(np.median(us(rt[:, 3] - rt[:, 2]))), 2),
         "gap_us": round(float(np.median(us(np.array(gaps)))), 2) if gaps else None,
         "cycles_per_ktile": round(float(np.median(kloop_ct / np.maximum(nk, 1))), 0),
@@ -853,6 +863,22 @@ def timeline_report(torch, coda, synth, out=None):
         fused()
     tl = TimelineRunner(torch, coda)
     fused(tl)
+    # The SwiGLU backward beside its epilogue-overlapped form, at the block's
+    # MLP shape and at the 1B-like one (seeded synthetic operands).
+    g = torch.Generator(device="cuda").manual_seed(5)
+    bf = torch.bfloat16
+    for (Mx, dx, Fx) in ((M, d, F), (8192, 2048, 8192)):
+        dO = torch.randn(Mx, dx, device="cuda", generator=g).to(bf)
+        Wd = (torch.randn(Fx, dx, device="cuda", generator=g) * Fx ** -0.5).to(bf)
+        pre = torch.randn(Mx, 2 * Fx, device="cuda", generator=g).to(bf)
+        dpre = torch.empty(Mx, 2 * Fx, dtype=bf, device="cuda")
+        sp = torch.empty(Mx, coda.coda_nparts(Fx), device="cuda")
+        for name, fn in (("swiglu_bwd+s", coda.coda_gemm_swiglu_bwd),
+                         ("swiglu_bwd+s overlap", coda.coda_gemm_swiglu_bwd_overlap)):
+            for _ in range(2):
+                fn(dO, Wd, pre, dpre, sp)
+            tl.run(f"{name} {Mx}x{Fx}x{dx}", lambda: fn(dO, Wd, pre, dpre, sp))
+        del dO, Wd, pre, dpre, sp
     lines = []
     for name, rows in tl.rows.items():
         for i, r in enumerate(rows):

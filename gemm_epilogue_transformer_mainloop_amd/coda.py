@@ -39,6 +39,7 @@ _SIGS = {
     "coda_mparts": (I, [I]),
     "coda_tile_split": (I, [I, I, I]),
     "coda_tile_split_tokens": (I, [I, I, I]),
+    "coda_swiglu_bwd_units": (I, [I, I, I, I]),
     "coda_lmhead_ce_workspace": (SZ, [I, I]),
     "coda_lmhead_ce_bwd_workspace": (SZ, [I, I, I]),
     "coda_gemm": (I, [P, I, P, I, P, I, I, I, I, P]),
@@ -50,6 +51,7 @@ _SIGS = {
     "coda_gemm_swiglu": (I, [P, I, P, I, P, P, I, P, I, I, I, I, P]),
     "coda_lmhead_ce": (I, [P, I, P, I, P, P, P, P, P, SZ, I, I, I, P]),
     "coda_gemm_swiglu_bwd": (I, [P, I, P, I, P, I, P, I, P, I, I, I, P]),
+    "coda_gemm_swiglu_bwd_overlap": (I, [P, I, P, I, P, I, P, I, P, I, I, I, P]),
     "coda_row_rms_bwd": (I, [P, I, I, I, P, P]),
     "coda_gemm_rowscale_bwd": (I, [P, I, P, I, P, I, P, P, P, P, I, P, I, P, I, P, I, I, I, P]),
     "coda_col_reduce": (I, [P, I, I, P, P]),
@@ -193,6 +195,10 @@ def coda_tile_split_tokens(F: int, T: int, cus: int) -> int:
     return int(lib().coda_tile_split_tokens(F, T, cus))
 
 
+def coda_swiglu_bwd_units(M: int, F: int, N: int, cus: int) -> int:
+    return int(lib().coda_swiglu_bwd_units(M, F, N, cus))
+
+
 def coda_lmhead_ce_workspace(M: int, V: int) -> int:
     return int(lib().coda_lmhead_ce_workspace(M, V))
 
@@ -334,7 +340,7 @@ def coda_lmhead_ce_logits(H, W, labels, lse=None, loss_row=None, loss_mean=None,
 # ----------------------------------------------------------------------------
 
 
-def coda_gemm_swiglu_bwd(dOut, Wd, Pre, dPre=None, spart=None, want_spart=True):
+def _swiglu_bwd(name, dOut, Wd, Pre, dPre, spart, want_spart):
     M, N = dOut.shape
     F = Wd.shape[0]
     if dPre is None:
@@ -342,9 +348,17 @@ def coda_gemm_swiglu_bwd(dOut, Wd, Pre, dPre=None, spart=None, want_spart=True):
     if spart is None and want_spart:
         spart = _empty((M, coda_nparts(F)), torch.float32, dOut)
     _dense(spart, "spart")
-    _call("coda_gemm_swiglu_bwd", _ptr(dOut), _ld(dOut), _ptr(Wd), _ld(Wd), _ptr(Pre), _ld(Pre), _ptr(dPre),
-          _ld(dPre), _ptr(spart), M, F, N, _stream())
+    _call(name, _ptr(dOut), _ld(dOut), _ptr(Wd), _ld(Wd), _ptr(Pre), _ld(Pre), _ptr(dPre), _ld(dPre), _ptr(spart),
+          M, F, N, _stream())
     return dPre, spart
+
+
+def coda_gemm_swiglu_bwd(dOut, Wd, Pre, dPre=None, spart=None, want_spart=True):
+    return _swiglu_bwd("coda_gemm_swiglu_bwd", dOut, Wd, Pre, dPre, spart, want_spart)
+
+
+def coda_gemm_swiglu_bwd_overlap(dOut, Wd, Pre, dPre=None, spart=None, want_spart=True):
+    return _swiglu_bwd("coda_gemm_swiglu_bwd_overlap", dOut, Wd, Pre, dPre, spart, want_spart)
 
 
 def coda_row_rms_bwd(spart, d: int, s=None):

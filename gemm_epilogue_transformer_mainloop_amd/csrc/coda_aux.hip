@@ -118,6 +118,16 @@ int coda_tile_split_tokens(int F, int T, int cus) {
   return token_split(nTF, nTT, T, cus);
 }
 
+int coda_swiglu_bwd_units(int M, int F, int N, int cus) {
+  if (M <= 0 || F <= 0 || N <= 0 || cus < 8) return 0;
+  const int nTF = cdiv(F, 256), nTT = cdiv(M, 256);
+  if (coda_tile_split(F, M, cus) > 0 || coda_tile_split_tokens(F, M, cus) > 0) return 0;
+  if (2 * nTF * nTT <= cus && cdiv(M, 128) > nTT) return 0;  // all 256 x 128 tiles
+  if ((long long)nTF * nTT <= cus) return 0;                  // a single round: nothing to overlap
+  const int nk = cdiv(N, 64);
+  return nk >= 64 ? 1 : nk >= 32 ? 2 : 0;
+}
+
 
 coda_status coda_row_rms(const float* part, int nparts, int M, int d, float eps, float* r,
                          hipStream_t stream) {

@@ -19,10 +19,11 @@ using namespace coda_launch;
 
 extern "C" {
 
-coda_status coda_gemm_swiglu_bwd(const coda_bf16* dOut, int ldd, const coda_bf16* Wd, int ldw,
-                                 const coda_bf16* Pre, int ldp, coda_bf16* dPre, int lddp,
-                                 float* spart, int M, int F, int N, hipStream_t stream) {
-  trace("coda_gemm_swiglu_bwd", "M=%d F=%d N=%d spart=%d", M, F, N, spart != nullptr);
+// The SwiGLU backward call's arguments, checked; CODA_OK to launch (or the
+// status to return, a no-op being CODA_OK with *empty set).
+static coda_status check_swiglu_bwd(const coda_bf16* dOut, int ldd, const coda_bf16* Wd, int ldw,
+                                    const coda_bf16* Pre, int ldp, coda_bf16* dPre, int lddp, float* spart,
+                                    int M, int F, int N, bool* empty) {
   Check c;
   c.shape(M >= 0 && F >= 0 && N >= 0 && F <= (1 << 29));
   if (c.st != CODA_OK) return c.st;
@@ -33,16 +34,51 @@ coda_status coda_gemm_swiglu_bwd(const coda_bf16* dOut, int ldd, const coda_bf16
   c.vec(spart, (long long)M * coda_nparts(F), 4, false);
   c.shape(F % 8 == 0 && N % 8 == 0);
   if (c.st != CODA_OK) return c.st;
-  if (M == 0 || F == 0) return CODA_OK;
-  if (coda_status s = c.device()) return s;
+  *empty = M == 0 || F == 0;
+  if (*empty) return CODA_OK;
+  return c.device();
+}
+
+// da[M x F] = dOut[M x N] Wd^T: features = F (rows of Wd, K-major), tokens = M.
+static coda_status launch_swiglu_bwd(const coda_bf16* dOut, int ldd, const coda_bf16* Wd, int ldw,
+                                     const coda_bf16* Pre, int ldp, coda_bf16* dPre, int lddp, float* spart,
+                                     int M, int F, int N, hipStream_t stream) {
   const int np = coda_nparts(F);
-  // da[M x F] = dOut[M x N] Wd^T: features = F (rows of Wd, K-major), tokens = M.
   if (spart) {
     EpiSwigluBwd<true> e{Pre, ldp, dPre, lddp, spart, np};
     return launch_gemm<true, true>(Wd, ldw, dOut, ldd, F, M, N, e, stream);
   }
   EpiSwigluBwd<false> e{Pre, ldp, dPre, lddp, nullptr, np};
   return launch_gemm<true, true>(Wd, ldw, dOut, ldd, F, M, N, e, stream);
+}
+
+coda_status coda_gemm_swiglu_bwd(const coda_bf16* dOut, int ldd, const coda_bf16* Wd, int ldw,
+                                 const coda_bf16* Pre, int ldp, coda_bf16* dPre, int lddp,
+                                 float* spart, int M, int F, int N, hipStream_t stream) {
+  trace("coda_gemm_swiglu_bwd", "M=%d F=%d N=%d spart=%d", M, F, N, spart != nullptr);
+  bool empty = false;
+  if (coda_status s = check_swiglu_bwd(dOut, ldd, Wd, ldw, Pre, ldp, dPre, lddp, spart, M, F, N, &empty)) return s;
+  if (empty) return CODA_OK;
+  return launch_swiglu_bwd(dOut, ldd, Wd, ldw, Pre, ldp, dPre, lddp, spart, M, F, N, stream);
+}
+
+coda_status coda_gemm_swiglu_bwd_overlap(const coda_bf16* dOut, int ldd, const coda_bf16* Wd, int ldw,
+                                         const coda_bf16* Pre, int ldp, coda_bf16* dPre, int lddp,
+                                         float* spart, int M, int F, int N, hipStream_t stream) {
+  trace("coda_gemm_swiglu_bwd_overlap", "M=%d F=%d N=%d spart=%d", M, F, N, spart != nullptr);
+  bool empty = false;
+  if (coda_status s = check_swiglu_bwd(dOut, ldd, Wd, ldw, Pre, ldp, dPre, lddp, spart, M, F, N, &empty)) return s;
+  if (empty) return CODA_OK;
+  const int units = coda_swiglu_bwd_units(M, F, N, device_cus());
+  if (units == 0) return launch_swiglu_bwd(dOut, ldd, Wd, ldw, Pre, ldp, dPre, lddp, spart, M, F, N, stream);
+  const Problem p = whole_problem(Wd, ldw, dOut, ldd, F, M, N, 256);
+  const EpiSwigluBwdDump dump{dPre, lddp};
+  const SwigluBwdCarryArgs ca{Pre, ldp, dPre, lddp, spart, coda_nparts(F), F, M};
+  if (spart)
+    return units == 1 ? launch_persistent<true, true, EpiSwigluBwdDump, SwigluBwdCarry<1, true>>(p, dump, ca, stream)
+                      : launch_persistent<true, true, EpiSwigluBwdDump, SwigluBwdCarry<2, true>>(p, dump, ca, stream);
+  return units == 1 ? launch_persistent<true, true, EpiSwigluBwdDump, SwigluBwdCarry<1, false>>(p, dump, ca, stream)
+                    : launch_persistent<true, true, EpiSwigluBwdDump, SwigluBwdCarry<2, false>>(p, dump, ca, stream);
 }
 
 coda_status coda_gemm_rowscale_bwd(const coda_bf16* dY, int ldd, const coda_bf16* W1, int ldw,

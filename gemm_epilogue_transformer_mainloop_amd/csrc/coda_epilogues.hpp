@@ -949,6 +949,252 @@ struct EpiSwigluBwd {
 };
 
 // ---------------------------------------------------------------------------
+// The same SwiGLU backward with the pair map of each tile run inside the next
+// tile's k-loop: epilogue/MFMA overlap within one wave (the PingPong overlap
+// of the epilogue with tensor-core work that the digg thread on CODA names;
+// paper Fig. 3).  A wave's 128 x 128 accumulator tile takes all 256 AGPRs,
+// so a second accumulator set does not fit; instead the tile's epilogue
+// (EpiSwigluBwdDump) stores da in fp32 where dpre will go: the 8 features
+// f..f+7 of one token that a lane holds as one accumulator run are 32 bytes
+// of fp32, exactly the 32 bytes of their 16 dpre values (columns 2f..2f+15).
+// The carry (SwigluBwdCarry) then runs that tile's pair map in 64 units per
+// wave during the next tile's k-loop, U units per k-tile: a unit is one
+// 16-byte chunk (4 pairs) of one run: a da load and a pre load during k-step
+// 0, the 4 pair maps between MFMA pairs of k-step 2 (after the k-loop's wait
+// for all memory operations, which covers the loads), the dpre store and the
+// s partial in k-step 3.  Each lane reads back only what it stored itself, at
+// the same addresses and in program order (as a register spill does).  Units
+// beyond what the k-loop holds, and the last tile's, run after it.
+// ---------------------------------------------------------------------------
+struct EpiSwigluBwdDump {
+  uint16_t* dpre;
+  int lddp;
+
+  template <int RI, int CI>
+  __device__ __forceinline__ void apply(const f32x16 (&acc)[RI][CI], const Geom& g) const {
+    const Lane L(g);
+    const TileView<2> d(dpre, lddp, g.tw0, 2 * g.fw0);
+#pragma unroll
+    for (int ci = 0; ci < CI; ++ci)
+#pragma unroll
+      for (int ri = 0; ri < RI; ++ri)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float v[8];
+          acc8(acc, ri, ci, h, v);
+          const bool ok = L.ok(ci, ri, h);
+          const int col = 2 * L.f(ri, h);
+          d.store16(L.t(ci), col, ok,
+                    (u32x4){__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+          d.store16(L.t(ci), col + 8, ok,
+                    (u32x4){__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
+        }
+  }
+};
+
+// The carry's arguments: the SwiGLU backward's pre, dpre and spart (nparts
+// per token) over F features and T tokens.
+struct SwigluBwdCarryArgs {
+  const uint16_t* pre;
+  int ldp;
+  uint16_t* dpre;
+  int lddp;
+  float* spart;
+  int nparts;
+  int F, T;
+};
+
+template <int U, bool HAS_SPART>
+struct SwigluBwdCarry {
+  static_assert(U == 1 || U == 2, "units per k-tile");
+  static constexpr bool kPersistent = true;
+  static constexpr int kPrimeOps = 2 * U;
+  // The dpre stores come last in a k-tile (k-step 3's last MFMA pair, after
+  // its DMA); the next k-tile's wait need not wait for their completion.
+  static constexpr int kTailOps = U;
+  static constexpr int UNITS = 64;  // per wave and 256 x 256 tile: 4 x 4 runs x 2 halves x 2 chunks
+  using Args = SwigluBwdCarryArgs;
+
+  Args a;
+  int lt, hh;
+  bool pending;      // a tile's pair map is outstanding
+  int tw0, fw0, pf;  // that tile's wave tile
+  int lim;           // units the current k-loop carries (the rest: drain)
+  __amdgpu_buffer_rsrc_t rp, rd;  // pre / dpre at its origin
+  u32x4 bd[U], bp[U];              // the next k-tile's units, in flight: da (fp32), pre (bf16 pairs)
+  // This k-tile's 4 U pairs, in flight through the pair map's stages.
+  float xa[U][4], xg[U][4], xu[U][4], xs[U][4], xt[U][4], xw[U][4];
+  uint32_t ow[U][4];               // dpre, packed
+  float pp[U];                     // the units' shares of the s statistic
+  float ss;                        // the s partial of the current token column
+
+  __device__ __forceinline__ explicit SwigluBwdCarry(const Args& args) : a(args) {
+    const int lane = (int)(threadIdx.x & 63);
+    lt = lane & 31;
+    hh = lane >> 5;
+    pending = false;
+    tw0 = fw0 = pf = 0;
+    lim = 0;
+    ss = 0.0f;
+    rp = rd = __builtin_amdgcn_make_buffer_rsrc((void*)a.dpre, (short)0, 0, 0x00020000);
+  }
+
+  // Unit u: token column ci, run (ri, half), chunk c (u = 16 ci + 4 ri + 2 half + c).
+  __device__ __forceinline__ bool unit(int u, int& t, int& col) const {
+    const int ci = (u >> 4) & 3, ri = (u >> 2) & 3, half = (u >> 1) & 1, c = u & 1;
+    t = ci * 32 + lt;
+    const int f = ri * 32 + half * 16 + hh * 8;
+    col = 2 * f + 8 * c;
+    return (int)pending & (int)(u < UNITS) & (int)(t < a.T - tw0) & (int)(f < a.F - fw0);
+  }
+  // An empty asm that takes x and gives it back: the value is computed here
+  // (the compiler would otherwise sink the whole pair map to its store, past
+  // every MFMA of the k-tile) and later stages cannot move above it.
+  __device__ __forceinline__ static void pin(float& x) { asm volatile("" : "+v"(x)); }
+  __device__ __forceinline__ static void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+  // The loads of unit u (none, by out-of-range offsets, beyond `end`).
+  __device__ __forceinline__ void load(int u, int end, u32x4& d, u32x4& q) const {
+    int t, col;
+    const bool ok = (int)unit(u, t, col) & (int)(u < end);
+    d = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, ok ? (uint32_t)(t * a.lddp + col) * 2u : OOB, 0, 0));
+    q = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, ok ? (uint32_t)(t * a.ldp + col) * 2u : OOB, 0, 2));
+  }
+  // Pair map stage k (0..7) of pair i of unit j, with (g, v) the pre pair,
+  // da the accumulator value, s = sigmoid(g) and t = g s:
+  //   du = da t,  dg = da v (s + t (1 - s)),  part += dg g + du v.
+  // Each stage depends only on earlier ones, so stage k of all 4 U pairs are
+  // independent instructions and one stage per MFMA pair keeps the wave's
+  // in-order issue from waiting on a result.
+  template <bool PIN = true>
+  __device__ __forceinline__ void stage(int k, int j, int i, const u32x4& d, const u32x4& q) {
+    switch (k) {
+      case 0:
+        xa[j][i] = __uint_as_float(d[i]);
+        xg[j][i] = bf_lo(q[i]);
+        xu[j][i] = bf_hi(q[i]);
+        if (PIN) pin(xa[j][i]), pin(xg[j][i]), pin(xu[j][i]);
+        break;
+      case 1:
+        xs[j][i] = fast_exp(-xg[j][i]);
+        if (PIN) pin(xs[j][i]);
+        break;
+      case 2:
+        xs[j][i] = __builtin_amdgcn_rcpf(1.0f + xs[j][i]);
+        if (PIN) pin(xs[j][i]);
+        break;
+      case 3:
+        xt[j][i] = xg[j][i] * xs[j][i];
+        if (PIN) pin(xt[j][i]);
+        break;
+      case 4:
+        xw[j][i] = fmaf(-xt[j][i], xs[j][i], xt[j][i]);
+        if (PIN) pin(xw[j][i]);
+        break;
+      case 5:
+        xw[j][i] += xs[j][i];
+        xt[j][i] *= xa[j][i];  // du
+        if (PIN) pin(xw[j][i]), pin(xt[j][i]);
+        break;
+      case 6:
+        xw[j][i] *= xa[j][i] * xu[j][i];  // dg
+        if (PIN) pin(xw[j][i]);
+        break;
+      default:
+        ow[j][i] = pack_bf16x2(xw[j][i], xt[j][i]);
+        pp[j] = fmaf(xw[j][i], xg[j][i], fmaf(xt[j][i], xu[j][i], i == 0 ? 0.0f : pp[j]));
+        if (PIN) pin(ow[j][i]), pin(pp[j]);
+        break;
+    }
+  }
+  __device__ __forceinline__ void store(int u, const uint32_t (&o)[4], float part) {
+    int t, col;
+    const bool ok = unit(u, t, col);
+    __builtin_amdgcn_raw_buffer_store_b128((u32x4){o[0], o[1], o[2], o[3]}, rd,
+                                           ok ? (uint32_t)(t * a.lddp + col) * 2u : OOB, 0, 2);
+    if constexpr (HAS_SPART) {
+      ss += ok ? part : 0.0f;
+      if ((u & 15) == 15) {  // the column's last unit (uniform)
+        const float s2 = sum_halves(ss);
+        ss = 0.0f;
+        if (pending && u < UNITS && hh == 0 && t < a.T - tw0 && a.F - fw0 > 0)
+          a.spart[(size_t)(tw0 + t) * a.nparts + pf] = s2;
+      }
+    }
+  }
+
+  // Units 0..U-1 in flight before k-tile 0.
+  __device__ __forceinline__ void prime(int nk) {
+    lim = nk * U < UNITS ? nk * U : UNITS;
+#pragma unroll
+    for (int j = 0; j < U; ++j) load(j, lim, bd[j], bp[j]);
+  }
+  // k-tile kt: at the start of k-step 2 (its loads have landed: the k-loop
+  // waited for every memory operation) units kt U + j enter the pair map and
+  // the next k-tile's go in flight; pair-map stage k runs at position 2 k of
+  // the 16 MFMA pairs of k-steps 2 and 3, the stores at the last.
+  __device__ __forceinline__ void slot(int kt, int step, int pr) {
+    if (step < 2) return;
+    const int pos = (step - 2) * 8 + pr;
+    if (pos == 0) {
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) stage(0, j, i, bd[j], bp[j]);
+#pragma unroll
+      for (int j = 0; j < U; ++j) load((kt + 1) * U + j, lim, bd[j], bp[j]);
+    } else if ((pos & 1) == 0) {
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) stage(pos >> 1, j, i, bd[j], bp[j]);
+    } else if (pos == 15) {
+#pragma unroll
+      for (int j = 0; j < U; ++j) store(kt * U + j, ow[j], pp[j]);
+    }
+  }
+
+  // Units u0 .. UNITS-1 of the pending tile, eight at a time.
+  __device__ __forceinline__ void serial(int u0) {
+    for (int u = u0; u < UNITS; u += 4 * U) {
+      u32x4 d[4][U], q[4][U];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int j = 0; j < U; ++j) load(u + b * U + j, UNITS, d[b][j], q[b][j]);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) stage<false>(k, j, i, d[b][j], q[b][j]);
+#pragma unroll
+        for (int j = 0; j < U; ++j) store(u + b * U + j, ow[j], pp[j]);
+      }
+    }
+  }
+  __device__ __forceinline__ void drain(int nk) {
+    const int done = nk * U < UNITS ? nk * U : UNITS;
+    if (pending && done < UNITS) serial(done);
+  }
+  __device__ __forceinline__ void pend(const Geom& g) {
+    pending = true;
+    tw0 = g.tw0;
+    fw0 = g.fw0;
+    pf = g.pf;
+    ss = 0.0f;
+    rp = __builtin_amdgcn_make_buffer_rsrc((void*)(a.pre + (size_t)tw0 * a.ldp + 2 * fw0), (short)0, 0x7fffffff,
+                                           0x00020000);
+    rd = __builtin_amdgcn_make_buffer_rsrc((void*)(a.dpre + (size_t)tw0 * a.lddp + 2 * fw0), (short)0, 0x7fffffff,
+                                           0x00020000);
+  }
+  __device__ __forceinline__ void finish() {
+    if (pending) serial(0);
+  }
+};
+
+// ---------------------------------------------------------------------------
 // RMSNorm backward epilogue with the delayed statistic (notes sec. 3):
 // acc = G = dY W1^T; dU = dRes + r (G * gamma) - r^2 s u; N2 = bf16(r u gamma);
 // gpart[pt, f] = sum over the wave's tokens of r G u (dgamma column partials).

@@ -68,10 +68,8 @@ inline int token_split(int nTF, int nTT, int T, int cus) {
   return split;
 }
 
-template <bool WK, bool XK, int BT = 256, class Epi>
-coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, int F, int T, int K,
-                        const Epi& epi, hipStream_t stream) {
-  constexpr int BF = 256;
+// The problem description of a launch over all of F x T.
+inline Problem whole_problem(const uint16_t* W, int ldw, const uint16_t* X, int ldx, int F, int T, int K, int BT) {
   Problem p;
   p.W = W;
   p.X = X;
@@ -80,7 +78,7 @@ coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, 
   p.F = F;
   p.T = T;
   p.K = K;
-  p.nTF = cdiv(F, BF);
+  p.nTF = cdiv(F, 256);
   p.nTT = cdiv(T, BT);
   p.f_base = 0;
   p.t_base = 0;
@@ -91,6 +89,29 @@ coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, 
     p.tl = g_tl_buf;
     p.tl_waves = g_tl_waves;
   }
+  return p;
+}
+
+// Persistent launch (gemm_epi_kernel_persistent) of p's 256 x 256 tiles on
+// the largest multiple of 8 workgroups not above the CU count, the carry
+// built from `ca` in every workgroup.  The caller has checked the plan
+// (coda_swiglu_bwd_units).
+template <bool WK, bool XK, class Epi, class Carry>
+coda_status launch_persistent(const Problem& p, const Epi& epi, const typename Carry::Args& ca, hipStream_t stream) {
+  const int nb = p.nTF * p.nTT;
+  const int g = (device_cus() / 8) * 8;
+  if (nb == 0) return CODA_OK;
+  if (g < 8) return CODA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((gemm_epi_kernel_persistent<WK, XK, Epi, Carry>), dim3(nb < g ? nb : g), dim3(NT), 0, stream,
+                     p, epi, ca);
+  return launched();
+}
+
+template <bool WK, bool XK, int BT = 256, class Epi>
+coda_status launch_gemm(const uint16_t* W, int ldw, const uint16_t* X, int ldx, int F, int T, int K,
+                        const Epi& epi, hipStream_t stream) {
+  constexpr int BF = 256;
+  Problem p = whole_problem(W, ldw, X, ldx, F, T, K, BT);
   const int nb = p.nTF * p.nTT;
   if (nb == 0) return CODA_OK;
   if constexpr (BT == 256 && AnyWaveWidth<Epi>::value) {

@@ -275,15 +275,16 @@ struct Problem {
 };
 
 // Timeline mark `slot` (0 tile start, 1 k-loop start, 2 k-loop end, 3
-// epilogue end) of this wave: record blockIdx.x * 4 + wave holds the
+// epilogue end) of this wave: record blk * 4 + wave (blk: the dispatch block,
+// or the tile of a persistent workgroup) holds the
 // reference-clock (100 MHz) stamps in words 0-3, the shader-clock stamps in
 // words 4-7, then the tile's token width, its k-tile count, and the HW_ID and
 // XCC_ID registers (which compute unit ran it).
-__device__ __forceinline__ void timeline_mark(const Problem& p, int slot, int bt, int nk) {
+__device__ __forceinline__ void timeline_mark(const Problem& p, int slot, int bt, int nk, int blk) {
   if constexpr (kTimeline) {
     const unsigned long long rt = __builtin_amdgcn_s_memrealtime();
     const unsigned long long ct = __builtin_amdgcn_s_memtime();
-    const int rec = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    const int rec = blk * 4 + (int)(threadIdx.x >> 6);
     if ((threadIdx.x & 63) == 0 && rec < p.tl_waves) {
       unsigned long long* r = p.tl + (size_t)rec * TL_WORDS;
       r[slot] = rt;
@@ -315,6 +316,25 @@ template <class G>
 __device__ __forceinline__ int feat_of(const G& g, int ri, int half) {
   return g.fw0 + ri * 32 + half * 16 + g.hh * 8;
 }
+
+// What the k-loop carries besides the GEMM: by default nothing.  A carry's
+// prime(nk) runs in the prologue, after the first two k-tiles' DMA (its
+// kPrimeOps memory operations are the last ones the prologue's wait allows in
+// flight); slot(kt, step, pr) runs after MFMA pair pr of k-step `step` (0..3)
+// of k-tile kt, inside that pair's scheduling fence; its last kTailOps memory
+// operations of a k-tile (stores, issued after the k-tile's DMA) stay in
+// flight through the next k-tile's wait; drain(nk) runs after the k-loop,
+// pend(g) after the epilogue.  kPersistent: one workgroup runs several tiles
+// (timeline records are then kept per tile, not per workgroup).
+struct NoCarry {
+  static constexpr bool kPersistent = false;
+  static constexpr int kPrimeOps = 0;  // memory operations prime() issues
+  static constexpr int kTailOps = 0;   // stores slot() issues after the k-tile's last DMA
+  __device__ __forceinline__ void prime(int) {}
+  __device__ __forceinline__ void slot(int, int, int) {}
+  __device__ __forceinline__ void drain(int) {}
+  __device__ __forceinline__ void pend(const Geom&) {}
+};
 
 // XCD-aware tile order: dispatch ids go round-robin over the 8 XCDs, so give
 // each XCD a contiguous range of tile ids, then walk tiles in groups of
@@ -353,8 +373,9 @@ constexpr int lds_bytes() {
 
 // One BF x BT output tile: block `bid` of `nb` blocks working on problem p,
 // with the workgroup's LDS at `smem` (lds_bytes<BF, BT, WK, XK>() bytes).
-template <int BF, int BT, bool WK, bool XK, class Epi>
-__device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, char* smem, int bid, int nb) {
+template <int BF, int BT, bool WK, bool XK, class Epi, class Carry>
+__device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, char* smem, int bid, int nb,
+                                              Carry& carry) {
   static_assert(BF == 256 && (BT == 256 || BT == 128), "tile shape");
   constexpr int WGF = 2, WGT = 2;           // 2 x 2 waves
   constexpr int WF = BF / WGF, WT = BT / WGT;
@@ -366,7 +387,11 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
   constexpr int A_REG = OA::REGION, B_REG = OB::REGION, B_OFF = 2 * A_REG;
   constexpr int A_PITCH = 2 * BF, B_PITCH = 2 * BT;  // MN-major k-row bytes
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  int tid = threadIdx.x;
+  // A persistent workgroup recomputes its per-lane offsets for every tile
+  // rather than keeping them live across the epilogue and the carry's work.
+  if constexpr (Carry::kPersistent) asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf = wave % WGF, wt = wave / WGF;
   const int lt = lane & 31, hh = lane >> 5;
@@ -396,7 +421,8 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
   const uint32_t lds0 = lds_addr(smem);
 
   const int nk = (p.K + BK - 1) / BK;
-  timeline_mark(p, 0, BT, nk);
+  const int blk = Carry::kPersistent ? bid : (int)blockIdx.x;
+  timeline_mark(p, 0, BT, nk, blk);
   const bool interior = f0 + BF <= p.F && t0 + BT <= p.T && p.K % BK == 0;
 
   constexpr int NP = RI * CI / 2;           // MFMA pairs per k-step
@@ -519,8 +545,10 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
         for (int d = 0; d < NE; ++d) dma_part(BK, 1, 0, d);
 #pragma unroll
         for (int d = 0; d < NL; ++d) dma_part(BK, 1, 1, d);
-        wait_vmcnt<NDMA>();
+        carry.prime(nk);
+        wait_vmcnt<NDMA + Carry::kPrimeOps>();
       } else {
+        carry.prime(nk);
         wait_vmcnt<0>();
       }
       __syncthreads();
@@ -550,6 +578,7 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
 #pragma unroll
         for (int r = 0; r < RPP; ++r) read_one(ST, 2, pr * RPP + r, fa2, fb2);
         if constexpr (HAS2 && NE > 0) dma_window(k2, ST, 0, pr);
+        carry.slot(kt, 0, pr);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -558,10 +587,11 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
 #pragma unroll
         for (int r = 0; r < RPP; ++r) read_one(ST, 3, pr * RPP + r, fa3, fb3);
         if constexpr (HAS2 && NE > 0) dma_window(k2, ST, 0, NP + pr);
+        carry.slot(kt, 1, pr);
         __builtin_amdgcn_sched_barrier(0);
       }
       // k-tile kt+1 has landed; the early part of kt+2 may still be in flight.
-      if constexpr (HAS1) wait_vmcnt<HAS2 ? NE : 0>();
+      if constexpr (HAS1) wait_vmcnt<(HAS2 ? NE : 0) + Carry::kTailOps>();
       __syncthreads();
 #pragma unroll
       for (int pr = 0; pr < NP; ++pr) {
@@ -571,6 +601,7 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
           for (int r = 0; r < RPP; ++r) read_one(NS, 0, pr * RPP + r, fa0, fb0);
         }
         if constexpr (HAS2) dma_window(k2, ST, 1, pr);
+        carry.slot(kt, 2, pr);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -581,13 +612,14 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
           for (int r = 0; r < RPP; ++r) read_one(NS, 1, pr * RPP + r, fa1, fb1);
         }
         if constexpr (HAS2) dma_window(k2, ST, 1, NP + pr);
+        carry.slot(kt, 3, pr);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
     // k-tile kt lives in LDS stage kt & 1.
-    timeline_mark(p, 1, BT, nk);
+    timeline_mark(p, 1, BT, nk, blk);
     int kt = 0;
     for (; kt + 2 < nk; ++kt) ktile(kt, T_{}, T_{});
     if (kt + 1 < nk) ktile(kt++, T_{}, F_{});
@@ -597,7 +629,8 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
     mainloop(std::false_type{});
   else
     mainloop(std::true_type{});
-  timeline_mark(p, 2, BT, nk);
+  timeline_mark(p, 2, BT, nk, blk);
+  carry.drain(nk);
 
   // The epilogues copy accumulators out of their AGPRs with inline asm, which
   // the compiler's hazard check does not see: 24 wait states cover the
@@ -619,7 +652,8 @@ __device__ __forceinline__ void gemm_epi_tile(const Problem& p, const Epi& epi, 
   } else {
     epi.template apply<RI, CI>(acc, g);
   }
-  timeline_mark(p, 3, BT, nk);
+  carry.pend(g);
+  timeline_mark(p, 3, BT, nk, blk);
 }
 
 template <int BF, int BT, bool WK, bool XK, class Epi>
@@ -630,7 +664,8 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel(const Problem p, const Epi
                                                                        : lds_bytes<BF, BT, WK, XK>();
   static_assert(LDS <= 160 * 1024, "epilogue staging exceeds the LDS");
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
-  gemm_epi_tile<BF, BT, WK, XK, Epi>(p, epi, smem, blockIdx.x, gridDim.x);
+  NoCarry none;
+  gemm_epi_tile<BF, BT, WK, XK, Epi>(p, epi, smem, blockIdx.x, gridDim.x, none);
 }
 
 // Two tile shapes in one dispatch (tile-count split): blocks [0, nbig) cover
@@ -644,10 +679,30 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel_split(const Problem p, con
   static_assert(LDS <= 160 * 1024, "epilogue staging exceeds the LDS");
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
   const int nbig = p.nTF * p.nTT;
+  NoCarry none;
   if ((int)blockIdx.x < nbig)
-    gemm_epi_tile<256, 256, WK, XK, Epi>(p, epi, smem, blockIdx.x, nbig);
+    gemm_epi_tile<256, 256, WK, XK, Epi>(p, epi, smem, blockIdx.x, nbig, none);
   else
-    gemm_epi_tile<256, 128, WK, XK, Epi>(q, epi, smem, blockIdx.x - nbig, gridDim.x - nbig);
+    gemm_epi_tile<256, 128, WK, XK, Epi>(q, epi, smem, blockIdx.x - nbig, gridDim.x - nbig, none);
+}
+
+// Persistent form: workgroup b runs tiles b, b + G, b + 2G, ... (G =
+// gridDim.x, a multiple of 8, so each tile runs on the XCD tile_coords gives
+// it) of p's 256 x 256 tiles, and the carry takes work from one tile into the
+// next tile's k-loop; finish() completes the last tile's.  The epilogue works
+// from registers (no LDS staging).
+template <bool WK, bool XK, class Epi, class Carry>
+__global__ void __launch_bounds__(NT) gemm_epi_kernel_persistent(const Problem p, const Epi epi,
+                                                                 const typename Carry::Args ca) {
+  static_assert(EpiLds<Epi>::value == 0, "the persistent kernel's epilogue works from registers");
+  __shared__ __attribute__((aligned(1024))) char smem[lds_bytes<256, 256, WK, XK>()];
+  Carry carry(ca);
+  const int nb = p.nTF * p.nTT;
+  for (int tile = blockIdx.x; tile < nb; tile += gridDim.x) {
+    gemm_epi_tile<256, 256, WK, XK, Epi>(p, epi, smem, tile, nb, carry);
+    __syncthreads();  // every wave is done with the operand stages before the next prologue
+  }
+  carry.finish();
 }
 
 }  // namespace coda

@@ -114,6 +114,20 @@ int coda_tile_split(int F, int T, int cus);
  * coda_tile_split.  Host-only: touches no device. */
 int coda_tile_split_tokens(int F, int T, int cus);
 
+/* Plan of coda_gemm_swiglu_bwd_overlap for M tokens, F features and
+ * reduction length N on `cus` compute units: the number U (1 or 2) of
+ * pair-map units that each k-tile of the GEMM mainloop carries, or 0 for the
+ * plain kernel.  With U > 0 the call is a persistent kernel of one workgroup
+ * per compute unit, whose tile epilogue stores da in fp32 into the dPre
+ * bytes of that tile (32 bytes per token and 8 features either way), and
+ * whose next k-loop reads it back and applies the pair map in 64 units per
+ * wave, U per k-tile; the last tile's units run after its k-loop.  It
+ * applies when no tile split does (coda_tile_split,
+ * coda_tile_split_tokens, the 256 x 128 small-problem plan), the problem
+ * has more than one round of 256 x 256 tiles, and N >= 2048 (32 k-tiles of
+ * 64).  Host-only: touches no device. */
+int coda_swiglu_bwd_units(int M, int F, int N, int cus);
+
 /* Workspace bytes coda_lmhead_ce needs for M rows and vocabulary V: the
  * per-tile max and sum-exp statistics and the gathered target logits that
  * the epilogue writes and the auxiliary reduction combines (reading notes
@@ -239,6 +253,23 @@ coda_status coda_lmhead_ce_logits(const coda_bf16* H, int ldh, const coda_bf16* 
 coda_status coda_gemm_swiglu_bwd(const coda_bf16* dOut, int ldd, const coda_bf16* Wd, int ldw,
                                  const coda_bf16* Pre, int ldp, coda_bf16* dPre, int lddp,
                                  float* spart, int M, int F, int N, hipStream_t stream);
+
+/* coda_gemm_swiglu_bwd with each output tile's epilogue overlapped with the
+ * next tile's MFMA work: the PingPong overlap of epilogue and tensor-core
+ * work that the digg thread on CODA names (paper Figure 3: the epilogue is
+ * tile-local).  Same arguments, outputs and errors; dPre is also used as the
+ * tiles' staging: until the call completes it holds da in fp32 (the 8
+ * features f..f+7 of a token are 32 bytes either way), so it must not alias
+ * any input (as for every call).  Where coda_swiglu_bwd_units(M, F, N, CUs)
+ * is 0 it runs coda_gemm_swiglu_bwd's kernel.  Measured on gfx950 at the
+ * 1B- and 8B-like MLP shapes it is 1.5-2x slower than coda_gemm_swiglu_bwd:
+ * one wave per SIMD holds the 256 accumulators, and the pair map's VALU work
+ * placed between its MFMAs does not overlap them, while reading da back in
+ * the accumulator layout (32 bytes of each of 32 rows per load) costs more
+ * than the plain epilogue's staged row loads. */
+coda_status coda_gemm_swiglu_bwd_overlap(const coda_bf16* dOut, int ldd, const coda_bf16* Wd, int ldw,
+                                         const coda_bf16* Pre, int ldp, coda_bf16* dPre, int lddp,
+                                         float* spart, int M, int F, int N, hipStream_t stream);
 
 /* Auxiliary reduction of the RMSNorm backward statistic (reading notes
  * section 3): s_i = sum_p spart[i, p] / d, d = the RMSNorm width. */

@@ -265,6 +265,23 @@ def test_timeline_build_validation():
     assert T.coda_timeline_set(None, 0) == 0                       # uninstall
 
 
+def test_swiglu_bwd_units(L):
+    """The deferred SwiGLU-backward plan: 1 unit per k-tile from 64 k-tiles,
+    2 from 32, only for more than one round of 256 x 256 tiles that no tile
+    split touches."""
+    f = coda.coda_swiglu_bwd_units
+    assert f(8192, 14336, 4096, 256) == 1     # the 8B-like MLP: 1792 tiles, 64 k-tiles
+    assert f(8192, 8192, 2048, 256) == 2      # the 1B-like MLP: 1024 tiles, 32 k-tiles
+    assert f(5000, 5000, 4104, 256) == 1      # ragged: 400 tiles, 65 k-tiles
+    assert f(5000, 5000, 2056, 256) == 2
+    assert f(8192, 8192, 1024, 256) == 0      # 16 k-tiles cannot carry 64 units
+    assert f(512, 1024, 4096, 256) == 0       # a single round (all 256 x 128 tiles)
+    assert f(4096, 4096, 4096, 256) == 0      # exactly one round: nothing to overlap
+    assert f(8192, 3072, 2048, 256) == 0 and coda.coda_tile_split(3072, 8192, 256) > 0   # feature split
+    assert f(9000, 8192, 2056, 256) == 0 and coda.coda_tile_split_tokens(8192, 9000, 256) > 0  # token split
+    assert f(8192, 14336, 4096, 4) == 0 and f(0, 14336, 4096, 256) == 0 and f(8192, 14336, 0, 256) == 0
+
+
 def test_tile_split_tokens(L):
     """The token split: only when neither the feature split nor the all-half-
     tile plan applies, the largest token-tile count that saves 0.2 rounds."""

@@ -43,6 +43,19 @@ def test_timeline_summary_known_clocks():
     # span 1000 .. 5700 ticks = 47 us; four tiles of 23 us on two compute units
     assert s["span_us"] == pytest.approx(47.0)
     assert s["cu_busy"] == pytest.approx(4 * 23.0 / (2 * 47.0), abs=1e-3)
+    assert s["kloop_us_first_round"] == pytest.approx(16.0)
+    assert s["kloop_us_later_rounds"] == pytest.approx(16.0)
+
+
+def test_timeline_summary_rounds():
+    """The first round of tiles (one per compute unit) is reported apart from
+    the later ones: here the later tiles' k-loops take 4 us longer."""
+    r = _records()
+    r[8:, 2] += 400                            # tiles 3 and 4 (records 8..15): k-loop end 4 us later
+    r[8:, 3] += 400
+    s = bench.timeline_summary(r)
+    assert s["kloop_us_first_round"] == pytest.approx(16.0)
+    assert s["kloop_us_later_rounds"] == pytest.approx(20.0)
 
 
 def test_timeline_summary_half_tiles():
