@@ -33,6 +33,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -52,12 +53,32 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def src_hash() -> str:
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_text(src: str) -> str:
+    """C++ source without its comments and with runs of whitespace folded
+    (string literals kept), so that edits to comments alone leave it equal."""
+    out = _CODE_TOKENS.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", src)
+    return " ".join(out.split())
+
+
+def src_hash(files=None) -> str:
+    """Hash of the kernel sources (csrc/, comments and layout ignored): a
+    measurement taken at one hash belongs to the kernels of that hash.
+    files: optional {name: text} to hash instead of the tree's csrc/."""
+    if files is None:
+        csrc = os.path.join(ROOT, "gemm_epilogue_transformer_mainloop_amd", "csrc")
+        files = {}
+        for name in sorted(os.listdir(csrc)):
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                files[name] = f.read()
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "gemm_epilogue_transformer_mainloop_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
+    for name in sorted(files):
+        h.update(name.encode())
+        h.update(b"\0")
+        h.update(code_text(files[name]).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

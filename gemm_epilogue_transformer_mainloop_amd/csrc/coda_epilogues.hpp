@@ -950,9 +950,9 @@ struct EpiSwigluBwd {
 
 // ---------------------------------------------------------------------------
 // The same SwiGLU backward with the pair map of each tile run inside the next
-// tile's k-loop: epilogue/MFMA overlap within one wave (the PingPong overlap
-// of the epilogue with tensor-core work that the digg thread on CODA names;
-// paper Fig. 3).  A wave's 128 x 128 accumulator tile takes all 256 AGPRs,
+// tile's k-loop: epilogue/MFMA overlap within one wave (the PingPong-style
+// overlap of the epilogue with tensor-core work that the social thread "CODA
+// reparameterizes memory-bound operations" names; paper Fig. 3).  A wave's 128 x 128 accumulator tile takes all 256 AGPRs,
 // so a second accumulator set does not fit; instead the tile's epilogue
 // (EpiSwigluBwdDump) stores da in fp32 where dpre will go: the 8 features
 // f..f+7 of one token that a lane holds as one accumulator run are 32 bytes

@@ -255,8 +255,9 @@ coda_status coda_gemm_swiglu_bwd(const coda_bf16* dOut, int ldd, const coda_bf16
                                  float* spart, int M, int F, int N, hipStream_t stream);
 
 /* coda_gemm_swiglu_bwd with each output tile's epilogue overlapped with the
- * next tile's MFMA work: the PingPong overlap of epilogue and tensor-core
- * work that the digg thread on CODA names (paper Figure 3: the epilogue is
+ * next tile's MFMA work: the PingPong-style overlap of epilogue and
+ * tensor-core work that the social thread "CODA reparameterizes
+ * memory-bound operations" names (paper Figure 3: the epilogue is
  * tile-local).  Same arguments, outputs and errors; dPre is also used as the
  * tiles' staging: until the call completes it holds da in fp32 (the 8
  * features f..f+7 of a token are 32 bytes either way), so it must not alias

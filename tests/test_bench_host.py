@@ -96,3 +96,16 @@ def test_traffic_entry_needs_current_source(tmp_path, monkeypatch):
     (prof / "traffic.json").write_text(json.dumps(ent))
     assert bench.load_traffic("c5 swiglu") is None
     assert bench.load_traffic("missing") is None
+
+
+def test_src_hash_ignores_comments():
+    """The kernel-source hash changes with the code, not with its comments
+    or layout (a measurement stays valid across a comment edit)."""
+    a = {"k.hpp": 'int f(int x) { return x + 1; }  // add one\n/* note */ const char* s = "a//b";\n'}
+    b = {"k.hpp": '/* other words */\nint f(int x) {\n  return x + 1;   // plus one\n}\nconst char* s = "a//b";\n'}
+    c = {"k.hpp": 'int f(int x) { return x + 2; }\nconst char* s = "a//b";\n'}
+    d = {"k.hpp": 'int f(int x) { return x + 1; }\nconst char* s = "a/ /b";\n'}
+    assert bench.src_hash(a) == bench.src_hash(b)
+    assert bench.src_hash(a) != bench.src_hash(c)
+    assert bench.src_hash(a) != bench.src_hash(d)      # string literals are code
+    assert bench.src_hash(a) != bench.src_hash({"j.hpp": a["k.hpp"]})
