@@ -952,19 +952,21 @@ struct EpiSwigluBwd {
 // The same SwiGLU backward with the pair map of each tile run inside the next
 // tile's k-loop: epilogue/MFMA overlap within one wave (the PingPong-style
 // overlap of the epilogue with tensor-core work that the social thread "CODA
-// reparameterizes memory-bound operations" names; paper Fig. 3).  A wave's 128 x 128 accumulator tile takes all 256 AGPRs,
-// so a second accumulator set does not fit; instead the tile's epilogue
-// (EpiSwigluBwdDump) stores da in fp32 where dpre will go: the 8 features
-// f..f+7 of one token that a lane holds as one accumulator run are 32 bytes
-// of fp32, exactly the 32 bytes of their 16 dpre values (columns 2f..2f+15).
-// The carry (SwigluBwdCarry) then runs that tile's pair map in 64 units per
-// wave during the next tile's k-loop, U units per k-tile: a unit is one
-// 16-byte chunk (4 pairs) of one run: a da load and a pre load during k-step
-// 0, the 4 pair maps between MFMA pairs of k-step 2 (after the k-loop's wait
-// for all memory operations, which covers the loads), the dpre store and the
-// s partial in k-step 3.  Each lane reads back only what it stored itself, at
-// the same addresses and in program order (as a register spill does).  Units
-// beyond what the k-loop holds, and the last tile's, run after it.
+// reparameterizes memory-bound operations" names; paper Fig. 3).  A wave's
+// 128 x 128 accumulator tile takes all 256 AGPRs, so a second accumulator set
+// does not fit; instead the tile's epilogue (EpiSwigluBwdDump) stores da in
+// fp32 where dpre will go: the 8 features f..f+7 of one token that a lane
+// holds as one accumulator run are 32 bytes of fp32, exactly the 32 bytes of
+// their 16 dpre values (columns 2f..2f+15).  The carry (SwigluBwdCarry) then
+// runs that tile's pair map in 64 units per wave during the next tile's
+// k-loop, U units per k-tile.  A unit is one 16-byte chunk (4 pairs) of one
+// run: its da and pre loads go out one k-tile ahead (at the start of k-step
+// 2, after the k-loop's wait for all memory operations, which covers the
+// previous k-tile's loads), its pair map runs in 8 stages between the MFMA
+// pairs of k-steps 2 and 3, and its dpre store and s partial come last.  Each
+// lane reads back only what it stored itself, at the same addresses and in
+// program order (as a register spill does).  Units beyond what the k-loop
+// holds, and the last tile's, run after it.
 // ---------------------------------------------------------------------------
 struct EpiSwigluBwdDump {
   uint16_t* dpre;
