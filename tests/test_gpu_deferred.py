@@ -7,7 +7,8 @@ plans it).
 Parity against the fp64 oracle on every output element, at shapes the plan
 routes to the deferred kernel (asserted; and one it does not, which runs the
 plain kernel): ragged tokens and features (partial
-wave tiles), a ragged reduction (masked last k-tile), one and two pair-map
+wave tiles, and waves with no token or no feature inside the matrix), a
+ragged reduction (masked last k-tile), one and two pair-map
 units per k-tile, 1.6 rounds of tiles (workgroups with one tile and with two)
 and 4 rounds, with and without the s partials.  dPre starts as NaN inside and
 a canary outside: every element must come out finite and the canary intact.
@@ -64,6 +65,7 @@ CASES = [
     (5000, 5000, 2048, 2, True),
     (5000, 5000, 4104, 1, True),
     (5000, 5000, 2056, 2, False),
+    (4200, 6208, 2048, 2, True),      # last tiles: a wave with no tokens, a wave with no features
     (8192, 8192, 2048, 2, True),
 ]
 
