@@ -875,6 +875,102 @@ def timeline_summary(rec):
     }
 
 
+# ----------------------------------------------------------------------------
+# board power and clocks under sustained load
+# ----------------------------------------------------------------------------
+
+
+def parse_smi_metric(text):
+    """Socket power (W) and the per-XCD graphics clocks (MHz) from the text of
+    `amd-smi metric -p -c`; None where absent."""
+    m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", text)
+    clocks = [float(c) for c in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", text)]
+    return {"socket_w": float(m.group(1)) if m else None, "gfx_mhz": clocks}
+
+
+def power_cap_w():
+    """The board's power cap (W) from `rocm-smi --showmaxpower`, or None."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showmaxpower"], capture_output=True, text=True, timeout=30).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    m = re.search(r"Max Graphics Package Power \(W\):\s*([0-9.]+)", out)
+    return float(m.group(1)) if m else None
+
+
+def power_report(torch, coda, synth, secs=12.0, out=None):
+    """Each of three loads runs for `secs` seconds while `amd-smi metric -p -c`
+    is sampled from a child process: the headline step, the plain GEMM of the
+    SwiGLU projection's shape (8192 x 28672 x 4096) and the MFMA-only clock
+    probe.  Samples from the first 3 s of each load are dropped."""
+    import subprocess
+    import threading
+
+    M, d, F = BLOCK_DIMS
+    bf = torch.bfloat16
+    p, T = block_inputs_device(torch, synth, M, d, F)
+    fused, _, _ = make_block(torch, coda, T, M, d, F, p["eps"])
+    g = torch.Generator(device="cuda").manual_seed(7)
+    h = torch.randn(M, d, device="cuda", generator=g).to(bf)
+    W = (torch.randn(d, 2 * F, device="cuda", generator=g) * d ** -0.5).to(bf)
+    Y = torch.empty(M, 2 * F, dtype=bf, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    probe_out = torch.zeros((cus, 2), dtype=torch.int64, device="cuda")
+    opf = block_op_flops(M, d, F)
+    loads = [
+        ("block step", fused, sum(opf[k] * BLOCK_LAUNCHES[k] for k in BLOCK_LAUNCHES)),
+        ("plain GEMM 8192x28672x4096", lambda: coda.coda_gemm(h, W, Y), 2.0 * M * 2 * F * d),
+        ("MFMA-only probe", lambda: coda.coda_probe_mfma(cus, 20000, probe_out), cus * 4 * 20000 * 8 * 32768.0),
+    ]
+    cap = power_cap_w()
+    lines = []
+    for name, fn, flops in loads:
+        samples, stop = [], threading.Event()
+        t_start = time.time()
+
+        def sample():
+            while not stop.is_set():
+                try:
+                    txt = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
+                                         timeout=20).stdout
+                except (OSError, subprocess.SubprocessError):
+                    return
+                if time.time() - t_start >= 3.0:
+                    samples.append(parse_smi_metric(txt))
+                stop.wait(1.0)
+
+        th = threading.Thread(target=sample, daemon=True)
+        fn()
+        torch.cuda.synchronize()
+        t_start = time.time()
+        th.start()
+        n = 0
+        while time.time() - t_start < secs:
+            fn()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        el = time.time() - t_start
+        stop.set()
+        th.join(timeout=30)
+        pw = [x["socket_w"] for x in samples if x["socket_w"] is not None]
+        ck = [float(np.mean(x["gfx_mhz"])) for x in samples if x["gfx_mhz"]]
+        ln = {"load": name, "seconds": round(el, 1), "calls": n, "tflops": round(flops * n / el / 1e12, 1),
+              "samples": len(samples), "power_cap_w": cap,
+              "socket_w_median": round(float(np.median(pw)), 1) if pw else None,
+              "socket_w_min": round(float(np.min(pw)), 1) if pw else None,
+              "socket_w_max": round(float(np.max(pw)), 1) if pw else None,
+              "gfx_mhz_median": round(float(np.median(ck)), 1) if ck else None}
+        print(json.dumps(ln), flush=True)
+        lines.append(ln)
+    if out:
+        with open(out, "w") as f:
+            for ln in lines:
+                f.write(json.dumps(ln) + "\n")
+
+
 def timeline_report(torch, coda, synth, out=None):
     """The headline step's GEMMs, one launch each with the tile timeline."""
     M, d, F = BLOCK_DIMS
@@ -927,6 +1023,9 @@ def main():
     ap.add_argument("--timeline", action="store_true",
                     help="only print per-tile timelines (prologue, k-loop, epilogue, shader clock) of the headline "
                          "step's GEMMs, from the timeline build libcoda_timeline.so")
+    ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
+                    help="only run the headline step, the plain GEMM of its largest shape and the MFMA-only probe "
+                         "for SECONDS each while sampling board power and clocks (amd-smi)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -950,6 +1049,10 @@ def main():
 
     if args.timeline:
         timeline_report(torch, coda, synth, args.out)
+        return
+
+    if args.power > 0:
+        power_report(torch, coda, synth, args.power, args.out)
         return
 
     if args.copy_calib:

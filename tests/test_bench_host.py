@@ -109,3 +109,27 @@ def test_src_hash_ignores_comments():
     assert bench.src_hash(a) != bench.src_hash(c)
     assert bench.src_hash(a) != bench.src_hash(d)      # string literals are code
     assert bench.src_hash(a) != bench.src_hash({"j.hpp": a["k.hpp"]})
+
+
+SMI_TEXT = """GPU: 0
+    POWER:
+        SOCKET_POWER: 1393 W
+        GFX_VOLTAGE: N/A
+    CLOCK:
+        GFX_0:
+            CLK: 1769 MHz
+            MIN_CLK: 500 MHz
+            MAX_CLK: 2400 MHz
+        GFX_1:
+            CLK: 1717 MHz
+            MIN_CLK: 500 MHz
+        MEM_0:
+            CLK: 2000 MHz
+"""
+
+
+def test_parse_smi_metric():
+    r = bench.parse_smi_metric(SMI_TEXT)
+    assert r["socket_w"] == 1393.0
+    assert r["gfx_mhz"] == [1769.0, 1717.0]          # graphics clocks only, not MIN/MAX or memory
+    assert bench.parse_smi_metric("no GPU") == {"socket_w": None, "gfx_mhz": []}
