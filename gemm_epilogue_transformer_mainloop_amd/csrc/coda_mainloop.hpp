@@ -687,10 +687,11 @@ __global__ void __launch_bounds__(NT) gemm_epi_kernel_split(const Problem p, con
 }
 
 // Persistent form: workgroup b runs tiles b, b + G, b + 2G, ... (G =
-// gridDim.x, a multiple of 8, so each tile runs on the XCD tile_coords gives
-// it) of p's 256 x 256 tiles, and the carry takes work from one tile into the
-// next tile's k-loop; finish() completes the last tile's.  The epilogue works
-// from registers (no LDS staging).
+// gridDim.x) of p's 256 x 256 tiles, and the carry takes work from one tile
+// into the next tile's k-loop; finish() completes the last tile's.  G is a
+// multiple of 8 whenever it is below the tile count, so every tile runs on the
+// XCD that tile_coords gives it.  The epilogue works from registers (no LDS
+// staging).
 template <bool WK, bool XK, class Epi, class Carry>
 __global__ void __launch_bounds__(NT) gemm_epi_kernel_persistent(const Problem p, const Epi epi,
                                                                  const typename Carry::Args ca) {
