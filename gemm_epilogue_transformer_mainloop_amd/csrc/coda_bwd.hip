@@ -62,10 +62,26 @@ coda_status coda_gemm_swiglu_bwd(const coda_bf16* dOut, int ldd, const coda_bf16
   return launch_swiglu_bwd(dOut, ldd, Wd, ldw, Pre, ldp, dPre, lddp, spart, M, F, N, stream);
 }
 
+// Whether the byte ranges of two row-major bf16 matrices (rows x cols, leading
+// dimension ld) intersect.
+static bool bmat_overlap(const coda_bf16* a, int lda, int arows, int acols, const coda_bf16* b, int ldb, int brows,
+                         int bcols) {
+  if (arows <= 0 || acols <= 0 || brows <= 0 || bcols <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, a1 = a0 + 2 * ((size_t)(arows - 1) * lda + acols);
+  const uintptr_t b0 = (uintptr_t)b, b1 = b0 + 2 * ((size_t)(brows - 1) * ldb + bcols);
+  return a0 < b1 && b0 < a1;
+}
+
 coda_status coda_gemm_swiglu_bwd_overlap(const coda_bf16* dOut, int ldd, const coda_bf16* Wd, int ldw,
                                          const coda_bf16* Pre, int ldp, coda_bf16* dPre, int lddp,
                                          float* spart, int M, int F, int N, hipStream_t stream) {
   trace("coda_gemm_swiglu_bwd_overlap", "M=%d F=%d N=%d spart=%d", M, F, N, spart != nullptr);
+  // dPre holds da in fp32 before the inputs are all read: it must not share
+  // a byte with them (checked here, since the result would be silently wrong).
+  if (dPre && (bmat_overlap(dPre, lddp, M, 2 * F, Pre, ldp, M, 2 * F) ||
+               bmat_overlap(dPre, lddp, M, 2 * F, dOut, ldd, M, N) ||
+               bmat_overlap(dPre, lddp, M, 2 * F, Wd, ldw, F, N)))
+    return CODA_ERR_SHAPE;
   bool empty = false;
   if (coda_status s = check_swiglu_bwd(dOut, ldd, Wd, ldw, Pre, ldp, dPre, lddp, spart, M, F, N, &empty)) return s;
   if (empty) return CODA_OK;

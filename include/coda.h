@@ -261,7 +261,8 @@ coda_status coda_gemm_swiglu_bwd(const coda_bf16* dOut, int ldd, const coda_bf16
  * tile-local).  Same arguments, outputs and errors; dPre is also used as the
  * tiles' staging: until the call completes it holds da in fp32 (the 8
  * features f..f+7 of a token are 32 bytes either way), so it must not alias
- * any input (as for every call).  Where coda_swiglu_bwd_units(M, F, N, CUs)
+ * any input (as for every call; here a dPre that shares a byte with dOut,
+ * Wd or Pre is rejected with CODA_ERR_SHAPE).  Where coda_swiglu_bwd_units(M, F, N, CUs)
  * is 0 it runs coda_gemm_swiglu_bwd's kernel.  Measured on gfx950 at the
  * 1B- and 8B-like MLP shapes it is 1.5-2x slower than coda_gemm_swiglu_bwd:
  * one wave per SIMD holds the 256 accumulators, and the pair map's VALU work

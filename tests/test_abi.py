@@ -265,6 +265,26 @@ def test_timeline_build_validation():
     assert T.coda_timeline_set(None, 0) == 0                       # uninstall
 
 
+def test_swiglu_bwd_overlap_rejects_aliasing(L):
+    """The epilogue-overlapped SwiGLU backward parks da in dPre before its
+    inputs are all read: a dPre sharing bytes with Pre, dOut or Wd is refused
+    before any device call; disjoint buffers pass this check (and fail later
+    only on the missing device or the fake pointers' other checks)."""
+    f = L.coda_gemm_swiglu_bwd_overlap
+    M, F, N = 16, 64, 64
+    big = ctypes.c_void_p(0x10000000)
+    # dPre == Pre (in place), dPre inside dOut, dPre overlapping Wd's last row
+    assert f(A16, N, A16b, N, big, 2 * F, big, 2 * F, None, M, F, N, None) == 2
+    assert f(big, 4096, A16b, N, A16c, 2 * F, ctypes.c_void_p(0x10000000 + 2 * 4096), 2 * F, None,
+             M, F, N, None) == 2
+    wd_end = 0x20000000 + 2 * ((F - 1) * N + N)
+    assert f(A16, N, ctypes.c_void_p(0x20000000), N, A16c, 2 * F, ctypes.c_void_p(wd_end - 16), 2 * F, None,
+             M, F, N, None) == 2
+    # adjacent but disjoint: not refused for aliasing
+    assert f(A16, N, ctypes.c_void_p(0x20000000), N, A16c, 2 * F, ctypes.c_void_p(wd_end), 2 * F, None,
+             M, F, N, None) != 2
+
+
 def test_swiglu_bwd_units(L):
     """The deferred SwiGLU-backward plan: 1 unit per k-tile from 64 k-tiles,
     2 from 32, only for more than one round of 256 x 256 tiles that no tile
