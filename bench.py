@@ -899,14 +899,58 @@ def power_cap_w():
     return float(m.group(1)) if m else None
 
 
-def power_report(torch, coda, synth, secs=12.0, out=None):
-    """Each of three loads runs for `secs` seconds while `amd-smi metric -p -c`
-    is sampled from a child process: the headline step, the plain GEMM of the
-    SwiGLU projection's shape (8192 x 28672 x 4096) and the MFMA-only clock
-    probe.  Samples from the first 3 s of each load are dropped."""
+def sustained_load(torch, fn, flops, secs, cap=None, settle=3.0):
+    """Run fn back to back for `secs` seconds while a child process samples
+    `amd-smi metric -p -c` about once a second (samples from the first
+    `settle` seconds dropped).  Returns the call rate, the TFLOP/s of `flops`
+    per call, and the median socket power and XCD clock (None where the tool
+    gives nothing)."""
     import subprocess
     import threading
 
+    samples, stop = [], threading.Event()
+    t_start = [time.time()]
+
+    def sample():
+        while not stop.is_set():
+            try:
+                txt = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
+                                     timeout=20).stdout
+            except (OSError, subprocess.SubprocessError):
+                return
+            if time.time() - t_start[0] >= settle:
+                samples.append(parse_smi_metric(txt))
+            stop.wait(1.0)
+
+    fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sample, daemon=True)
+    t_start[0] = time.time()
+    th.start()
+    n = 0
+    while time.time() - t_start[0] < secs:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    el = time.time() - t_start[0]
+    stop.set()
+    th.join(timeout=30)
+    pw = [x["socket_w"] for x in samples if x["socket_w"] is not None]
+    ck = [float(np.mean(x["gfx_mhz"])) for x in samples if x["gfx_mhz"]]
+    return {"seconds": round(el, 1), "calls": n, "tflops": round(flops * n / el / 1e12, 1), "samples": len(samples),
+            "power_cap_w": cap,
+            "socket_w_median": round(float(np.median(pw)), 1) if pw else None,
+            "socket_w_min": round(float(np.min(pw)), 1) if pw else None,
+            "socket_w_max": round(float(np.max(pw)), 1) if pw else None,
+            "gfx_mhz_median": round(float(np.median(ck)), 1) if ck else None}
+
+
+def power_report(torch, coda, synth, secs=12.0, out=None):
+    """The headline step, the plain GEMM of the SwiGLU projection's shape
+    (8192 x 28672 x 4096) and the MFMA-only clock probe, each under
+    sustained_load for `secs` seconds."""
     M, d, F = BLOCK_DIMS
     bf = torch.bfloat16
     p, T = block_inputs_device(torch, synth, M, d, F)
@@ -926,43 +970,7 @@ def power_report(torch, coda, synth, secs=12.0, out=None):
     cap = power_cap_w()
     lines = []
     for name, fn, flops in loads:
-        samples, stop = [], threading.Event()
-        t_start = time.time()
-
-        def sample():
-            while not stop.is_set():
-                try:
-                    txt = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
-                                         timeout=20).stdout
-                except (OSError, subprocess.SubprocessError):
-                    return
-                if time.time() - t_start >= 3.0:
-                    samples.append(parse_smi_metric(txt))
-                stop.wait(1.0)
-
-        th = threading.Thread(target=sample, daemon=True)
-        fn()
-        torch.cuda.synchronize()
-        t_start = time.time()
-        th.start()
-        n = 0
-        while time.time() - t_start < secs:
-            fn()
-            n += 1
-            if n % 4 == 0:
-                torch.cuda.synchronize()
-        torch.cuda.synchronize()
-        el = time.time() - t_start
-        stop.set()
-        th.join(timeout=30)
-        pw = [x["socket_w"] for x in samples if x["socket_w"] is not None]
-        ck = [float(np.mean(x["gfx_mhz"])) for x in samples if x["gfx_mhz"]]
-        ln = {"load": name, "seconds": round(el, 1), "calls": n, "tflops": round(flops * n / el / 1e12, 1),
-              "samples": len(samples), "power_cap_w": cap,
-              "socket_w_median": round(float(np.median(pw)), 1) if pw else None,
-              "socket_w_min": round(float(np.min(pw)), 1) if pw else None,
-              "socket_w_max": round(float(np.max(pw)), 1) if pw else None,
-              "gfx_mhz_median": round(float(np.median(ck)), 1) if ck else None}
+        ln = {"load": name, **sustained_load(torch, fn, flops, secs, cap)}
         print(json.dumps(ln), flush=True)
         lines.append(ln)
     if out:
@@ -1175,6 +1183,11 @@ def main():
                     for k, v in utm.stats_ms().items()},
         }
         log(f"unfused block: {ums:.3f} ms/step ({ums / ms_step:.3f}x the fused step)")
+        # Board power and clocks while the fused step runs for a few seconds
+        # (outside the timed region): the rate the step sustains at the cap.
+        line["board_power"] = {"load": "the fused step, back to back",
+                               **sustained_load(torch, fused, total_flops, 6.0, power_cap_w(), settle=2.0)}
+        log(f"board power: {line['board_power']}")
         line["cold_cache"] = {
             "working_set_bytes": int(ws_bytes),
             "note": f"the step touches {ws_bytes / 2 ** 30:.1f} GiB of weights, activations and gradients, far "
