@@ -1031,6 +1031,8 @@ def main():
     ap.add_argument("--timeline", action="store_true",
                     help="only print per-tile timelines (prologue, k-loop, epilogue, shader clock) of the headline "
                          "step's GEMMs, from the timeline build libcoda_timeline.so")
+    ap.add_argument("--no-power", action="store_true",
+                    help="no board_power sampling (amd-smi child processes), e.g. under a profiler")
     ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
                     help="only run the headline step, the plain GEMM of its largest shape and the MFMA-only probe "
                          "for SECONDS each while sampling board power and clocks (amd-smi)")
@@ -1185,9 +1187,10 @@ def main():
         log(f"unfused block: {ums:.3f} ms/step ({ums / ms_step:.3f}x the fused step)")
         # Board power and clocks while the fused step runs for a few seconds
         # (outside the timed region): the rate the step sustains at the cap.
-        line["board_power"] = {"load": "the fused step, back to back",
-                               **sustained_load(torch, fused, total_flops, 6.0, power_cap_w(), settle=2.0)}
-        log(f"board power: {line['board_power']}")
+        if not args.no_power:
+            line["board_power"] = {"load": "the fused step, back to back",
+                                   **sustained_load(torch, fused, total_flops, 6.0, power_cap_w(), settle=2.0)}
+            log(f"board power: {line['board_power']}")
         line["cold_cache"] = {
             "working_set_bytes": int(ws_bytes),
             "note": f"the step touches {ws_bytes / 2 ** 30:.1f} GiB of weights, activations and gradients, far "
