@@ -123,3 +123,43 @@ def test_swiglu_bwd_deferred_8b_rows():
     ref = O.swiglu_bwd(O.gemm(dOut.f64()[rows], Wd.f64().T), pre_r)
     assert_close(f64(dpre[idx]), ref, "dpre rows")
     assert_close(spart[idx].double().cpu().numpy(), spart_ref(ref, pre_r, coda.coda_nparts(F)), "spart rows")
+
+
+def _random_shapes(n=4, seed=2024):
+    """Seeded shapes (M in [3000, 9000), F and N multiples of 8) that the plan
+    routes to the overlapped kernel on this device: tile counts that leave
+    some workgroups one tile more than others."""
+    coda = C()
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.integers(3000, 9000))
+        F = int(rng.integers(300, 1400)) * 8
+        N = int(rng.integers(256, 700)) * 8
+        if coda.coda_swiglu_bwd_units(M, F, N, cus()) > 0:
+            out.append((M, F, N))
+    return out
+
+
+def test_swiglu_bwd_overlap_random_shapes():
+    """Every column of a seeded sample of rows against the oracle, and the s
+    partials, at four random shapes the plan accepts."""
+    coda = C()
+    for k, (M, F, N) in enumerate(_random_shapes()):
+        say(f"case: overlap random shape {k}: M={M} F={F} N={N} units={coda.coda_swiglu_bwd_units(M, F, N, cus())}")
+        seed = 7200 + 10 * k
+        dOut = S.normal_bf16(seed, (M, N))
+        Wd = S.normal_bf16(seed + 1, (F, N), std=F ** -0.5)
+        pre = S.normal_bf16(seed + 2, (M, 2 * F), std=2.0)
+        dpre = torch.full((M, 2 * F), float("nan"), dtype=torch.bfloat16, device="cuda")
+        dpre, spart = coda.coda_gemm_swiglu_bwd_overlap(dev(dOut), dev(Wd), dev(pre), dPre=dpre)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(dpre.float()).all()), "dPre has elements left unwritten"
+        rng = np.random.default_rng(seed)
+        rows = np.array(sorted(set([0, 255, 256, M - 1] + rng.choice(M, 12, replace=False).tolist())))
+        idx = torch.as_tensor(rows, device="cuda")
+        pre_r = pre.f64()[rows]
+        ref = O.swiglu_bwd(O.gemm(dOut.f64()[rows], Wd.f64().T), pre_r)
+        assert_close(f64(dpre[idx]), ref, "dpre rows")
+        assert_close(spart[idx].double().cpu().numpy(), spart_ref(ref, pre_r, coda.coda_nparts(F)), "spart rows")
+        del dOut, Wd, pre, dpre, spart
